@@ -1,0 +1,47 @@
+// Weighted combine of the routed experts' output rows and the shared expert
+// (gfx950).  For token t: y_t = sum_{j=0..topk-1} w[t, j] * o(t, j) + o_shared(t),
+// accumulated in fp32 in that fixed order, then rounded to bf16.  o(t, j) is
+// the down-projection row of pair t*topk + j, already scaled by the pair's
+// weight_scale_2; routing weights are applied here, after the down GEMM (the
+// "weighted combine" of the MoE layer; summation order is a reading).  A pair
+// whose expert id is outside [0, E) contributes nothing.
+#include "device_util.h"
+
+namespace nvfp4 {
+
+__global__ __launch_bounds__(256) void nvfp4_moe_combine(const CombineArgs a) {
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (n >= a.H) return;
+  const int P = a.T * a.topk;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < a.topk; ++j) {
+    const int id = a.ids[t * a.topk + j];
+    if (id < 0 || id >= a.E) continue;
+    const float w = a.w[t * a.topk + j];
+    const float4* src = reinterpret_cast<const float4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n);
+    const float4 v0 = src[0], v1 = src[1];
+    acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
+    acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+  }
+  if (a.shared) {
+    const float4* src = reinterpret_cast<const float4*>(a.slot + (int64_t)(P + t) * a.H + n);
+    const float4 v0 = src[0], v1 = src[1];
+    acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+    acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+  }
+  uint4 o;
+  o.x = float_to_bf16_bits(acc[0]) | (float_to_bf16_bits(acc[1]) << 16);
+  o.y = float_to_bf16_bits(acc[2]) | (float_to_bf16_bits(acc[3]) << 16);
+  o.z = float_to_bf16_bits(acc[4]) | (float_to_bf16_bits(acc[5]) << 16);
+  o.w = float_to_bf16_bits(acc[6]) | (float_to_bf16_bits(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(a.y + (int64_t)t * a.H + n) = o;
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  dim3 grid((a.H / 8 + 255) / 256, a.T);
+  hipLaunchKernelGGL(nvfp4_moe_combine, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

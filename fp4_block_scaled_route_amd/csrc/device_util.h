@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 NVFP4 kernels: exact E2M1/E4M3 decode
+// into fp16, round-to-nearest-even encoders, per-row power-of-two shifts.
+#pragma once
+
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+// 8 E2M1 codes (element e in nibble e of `w`) times one E4M3 block scale,
+// as 8 fp16.  Exact: |E2M1 * E4M3| lies in {0} U [2^-10, 2688] and needs at
+// most 5 significant bits, which fp16 holds.  The hardware converter applies
+// only the exponent of its scale operand, so the block scale is multiplied in
+// afterwards with one packed fp16 multiply per pair of elements.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, f16 s) {
+  f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  const f16x2 ss = {s, s};
+  a0 *= ss;
+  a1 *= ss;
+  a2 *= ss;
+  a3 *= ss;
+  return (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+// Four E4M3 scale bytes -> four fp16 values (exact: E4M3 fits fp16).
+__device__ __forceinline__ void scales4(uint32_t s, f16 (&out)[4]) {
+  f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
+  f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+__device__ __forceinline__ float e4m3_to_float(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// Round-to-nearest-even E4M3FN byte of a non-negative float, saturating at
+// 448 (0x7E).  Normal range: keep 3 mantissa bits with RNE on the 20 dropped
+// bits; subnormal range (< 2^-6): the byte is RNE(v * 2^9).
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;
+  const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+  const int e = (int)(b >> 23) - 127;
+  if (e < -6) return (uint32_t)__builtin_rintf(__uint_as_float(b) * 512.0f);  // 0..8; 8 = 2^-6
+  const uint32_t mant = b & 0x7FFFFFu;
+  const uint32_t keep = mant >> 20, rem = mant & 0xFFFFFu;
+  uint32_t code = ((uint32_t)(e + 7) << 3) | keep;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Round-to-nearest-even E2M1 code of a float, saturating at 6; the sign bit
+// is the float's sign bit.  Thresholds are the midpoints between the
+// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; at a midpoint the even code wins.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const float a = __builtin_fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Power-of-two shift that maps a row whose max |value| has the fp32 bit
+// pattern `mbits` into [2^14, 2^15): exact fp16 staging of bf16/fp32 rows.
+// Zero rows, and rows whose max is inf/NaN, get shift 0.
+__device__ __forceinline__ int shift_from_maxbits(uint32_t mbits) {
+  const uint32_t e = (mbits >> 23) & 0xFFu;
+  if (mbits == 0u || e == 0xFFu) return 0;
+  if (e == 0u) return 140;
+  return 141 - (int)e;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// bf16 round-to-nearest-even of a float (hardware conversion, NaN preserving).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float v) {
+  __bf16 b = (__bf16)v;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,232 @@
+// Token -> expert permutation for the grouped GEMM (gfx950).
+//
+// The grouped GEMM takes int32 segment offsets of the rows of each expert
+// (page "nvfp4-megamoe-kernel, commit 4c6464e - vllm", note on the custom-op
+// GEMM implementation).  Rows are the (token, slot) pairs f = t*topk + j,
+// grouped by expert id, stable in f; the shared expert's group of T rows
+// follows the routed groups.
+//
+// One workgroup of 16 waves does the whole permutation (P = T*topk pairs is
+// at most a few tens of thousands):
+//   1. wave w counts the ids of its contiguous segment of pairs into its own
+//      LDS histogram row (LDS atomics: order-free, exact);
+//   2. per expert, an exclusive scan over the 16 rows gives each wave's base
+//      inside the expert's group; an exclusive scan over experts gives the
+//      group offsets;
+//   3. each wave walks its segment 64 pairs at a time; lanes holding the same
+//      expert find each other with one ballot per id bit, rank themselves by
+//      lane order (so the order inside a group is the pair order), and the
+//      highest of them advances the wave's counter for that expert.
+// It also writes the processing order of the groups for the GEMM (non-empty
+// groups, largest first, ties by id) so that the GEMM grid needs no host
+// synchronisation.  Extra workgroups compute the per-row staging shifts of the
+// bf16 activations and clear the row-max buffer of the hidden activations.
+#include "device_util.h"
+
+namespace nvfp4 {
+
+namespace {
+constexpr int kPermWaves = 16;
+constexpr int kMaxExperts = 512;
+}  // namespace
+
+__device__ void rowshift_rows(const uint16_t* x, int rows, int cols, int* rowshift, int first_wave,
+                              int wave_stride) {
+  const int lane = threadIdx.x & 63;
+  for (int r = first_wave; r < rows; r += wave_stride) {
+    const uint16_t* row = x + (int64_t)r * cols;
+    uint32_t mx = 0;
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + c);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx = max(mx, u[e] & 0x7FFFu);
+        mx = max(mx, (u[e] >> 16) & 0x7FFFu);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if (lane == 0) rowshift[r] = shift_from_maxbits(mx << 16);
+  }
+}
+
+__global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
+  if (blockIdx.x > 0) {
+    // row shifts of x and clearing of the row-max buffer
+    const int nwav = (gridDim.x - 1) * (blockDim.x / 64);
+    const int w = (blockIdx.x - 1) * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (a.x) rowshift_rows(a.x, a.T, a.H, a.rowshift, w, nwav);
+    if (a.zero_buf)
+      for (int i = (blockIdx.x - 1) * blockDim.x + threadIdx.x; i < a.n_zero; i += (gridDim.x - 1) * blockDim.x)
+        a.zero_buf[i] = 0u;
+    return;
+  }
+
+  __shared__ int hist[kPermWaves][kMaxExperts];
+  __shared__ int goff[kMaxExperts + 2];
+  __shared__ int wsum[64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, P = a.T * a.topk;
+  const int seg = ((P + kPermWaves - 1) / kPermWaves + 63) & ~63;
+  const int f0 = wave * seg, f1 = min(P, f0 + seg);
+
+  for (int i = tid; i < kPermWaves * E; i += blockDim.x) hist[i / E][i % E] = 0;
+  __syncthreads();
+
+  // 1. per-wave histograms
+  for (int f = f0 + lane; f < f1; f += 64) {
+    const int id = a.ids[f];
+    if (id >= 0 && id < E) atomicAdd(&hist[wave][id], 1);
+  }
+  __syncthreads();
+
+  // 2a. per expert: exclusive scan over waves, totals into goff[e+1]
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w][e];
+      hist[w][e] = run;
+      run += c;
+    }
+    goff[e + 1] = run;
+  }
+  __syncthreads();
+  // 2b. exclusive scan of the totals (wave 0: each lane sums a contiguous piece)
+  if (wave == 0) {
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per, e1 = min(E, e0 + per);
+    int s = 0;
+    for (int e = e0; e < e1; ++e) s += goff[e + 1];
+    // inclusive scan of lane sums
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - s;
+    for (int e = e0; e < e1; ++e) {
+      const int c = goff[e + 1];
+      goff[e] = run;
+      run += c;
+    }
+    if (lane == 63) {
+      goff[E] = incl;                       // rows of valid routed pairs
+      goff[E + 1] = incl + (a.shared ? a.T : 0);
+    }
+  }
+  __syncthreads();
+
+  // 3. stable ranks
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    int id = f < f1 ? a.ids[f] : -1;
+    if (id < 0 || id >= E) id = -1;
+    uint64_t peers = __ballot(id >= 0);
+#pragma unroll 1
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bal = __ballot(id >= 0 && ((id >> b) & 1));
+      peers &= ((id >> b) & 1) ? bal : ~bal;
+    }
+    if (id >= 0) {
+      const uint64_t below = peers & ((1ull << lane) - 1ull);
+      const int rank = __popcll(below);
+      const int pos = goff[id] + hist[wave][id] + rank;
+      a.perm[pos] = f;
+      a.inv[f] = pos;
+      if (a.perm_out) a.perm_out[pos] = f;
+      if ((peers >> lane) == 1ull) hist[wave][id] += __popcll(peers);  // highest peer lane
+    } else if (f < f1) {
+      a.inv[f] = -1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // shared expert rows
+  const int pv = goff[E];
+  if (a.shared) {
+    for (int t = tid; t < a.T; t += blockDim.x) {
+      a.perm[pv + t] = P + t;
+      a.inv[P + t] = pv + t;
+      if (a.perm_out) a.perm_out[pv + t] = P + t;
+    }
+  }
+  for (int i = tid; i < E + 2; i += blockDim.x) {
+    a.offsets[i] = goff[i];
+    if (a.offsets_out) a.offsets_out[i] = goff[i];
+  }
+
+  // 4. group order: non-empty groups, largest first, ties by id
+  const int G = E + (a.shared ? 1 : 0);
+  for (int g = tid; g < G; g += blockDim.x) {
+    const int mg = goff[g + 1] - goff[g];
+    if (mg <= 0) continue;
+    int rank = 0;
+    for (int h = 0; h < G; ++h) {
+      const int mh = goff[h + 1] - goff[h];
+      rank += (mh > mg) || (mh == mg && h < g);
+    }
+    a.glist[rank] = g;
+  }
+  if (tid < 64) {
+    int cnt = 0;
+    for (int g = lane; g < G; g += 64) cnt += (goff[g + 1] - goff[g]) > 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) *a.gcount = cnt;
+  }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_rowshift_bf16(const uint16_t* x, int rows, int cols, int* rowshift) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  rowshift_rows(x, rows, cols, rowshift, w, gridDim.x * 4);
+}
+
+// gs = (max over rows of the row maxima) / 2688 for calibrating the global
+// scale of the hidden activations (page "commit 4c6464e", notes on warm-up
+// calibration of the activation global scale).
+__global__ __launch_bounds__(1024) void nvfp4_amax_to_gs(const unsigned* rowmax, int rows, float* gs_out) {
+  __shared__ unsigned wmax[16];
+  unsigned m = 0;
+  for (int i = threadIdx.x; i < rows; i += blockDim.x) m = max(m, rowmax[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned r = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r = max(r, wmax[w]);
+    gs_out[0] = __uint_as_float(r) / 2688.0f;
+  }
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  if (a.E > kMaxExperts) return hipErrorInvalidValue;
+  int extra = 0;
+  if (a.x || a.zero_buf) {
+    const int by_rows = a.x ? (a.T + 15) / 16 : 0;
+    const int by_zero = a.zero_buf ? (a.n_zero + 1023) / 1024 : 0;
+    extra = max(1, min(1024, max(by_rows, by_zero)));
+  }
+  hipLaunchKernelGGL(nvfp4_moe_permute, dim3(1 + extra), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowshift_bf16(const uint16_t* x, int rows, int cols, int* rowshift, hipStream_t s) {
+  const int grid = max(1, min(1024, (rows + 3) / 4));
+  hipLaunchKernelGGL(nvfp4_rowshift_bf16, dim3(grid), dim3(256), 0, s, x, rows, cols, rowshift);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_to_gs(const unsigned* rowmax, int rows, float* gs_out, hipStream_t s) {
+  hipLaunchKernelGGL(nvfp4_amax_to_gs, dim3(1), dim3(1024), 0, s, rowmax, rows, gs_out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

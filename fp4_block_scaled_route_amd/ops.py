@@ -1,0 +1,193 @@
+"""ctypes binding of libnvfp4.so (declared in include/nvfp4.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch is used for device memory (outputs and workspace are
+allocated here when the caller does not pass them) and for the current HIP
+stream.  If the library has not been built, every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+
+_c_i64 = ctypes.c_int64
+_c_ptr = ctypes.c_void_p
+
+EXPORTED = (
+    "nvfp4_status_string",
+    "nvfp4_abi_version",
+    "nvfp4_quantize_act",
+    "nvfp4_linear_workspace_size",
+    "nvfp4_linear",
+    "nvfp4_moe_workspace_size",
+    "nvfp4_moe_grouped",
+)
+ABI_VERSION = 1
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"nvfp4 status {status}: {msg}")
+        self.status = status
+
+
+class MoeArgs(ctypes.Structure):
+    """Mirror of nvfp4_moe_args (field order and types as in include/nvfp4.h)."""
+    _fields_ = [
+        ("T", _c_i64), ("H", _c_i64), ("I", _c_i64), ("E", _c_i64), ("topk", _c_i64),
+        ("x", _c_ptr), ("x_fp4", _c_ptr), ("x_sf", _c_ptr), ("a1_gs", _c_ptr),
+        ("a2_gs", _c_ptr), ("a2_gs_out", _c_ptr),
+        ("topk_ids", _c_ptr), ("topk_w", _c_ptr),
+        ("w1", _c_ptr), ("w1_sf", _c_ptr), ("w1_ws2", _c_ptr),
+        ("w2", _c_ptr), ("w2_sf", _c_ptr), ("w2_ws2", _c_ptr),
+        ("s1", _c_ptr), ("s1_sf", _c_ptr), ("s1_ws2", _c_ptr),
+        ("s2", _c_ptr), ("s2_sf", _c_ptr), ("s2_ws2", _c_ptr),
+        ("workspace", _c_ptr), ("workspace_bytes", ctypes.c_size_t),
+        ("offsets_out", _c_ptr), ("perm_out", _c_ptr),
+        ("y", _c_ptr),
+        ("stage_events", ctypes.POINTER(_c_ptr)),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnvfp4.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fp4_block_scaled_route_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_status_string.argtypes = [ctypes.c_int]
+        L.nvfp4_abi_version.restype = ctypes.c_int
+        L.nvfp4_abi_version.argtypes = []
+        L.nvfp4_quantize_act.restype = ctypes.c_int
+        L.nvfp4_quantize_act.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr]
+        L.nvfp4_linear_workspace_size.restype = ctypes.c_size_t
+        L.nvfp4_linear_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64]
+        L.nvfp4_linear.restype = ctypes.c_int
+        L.nvfp4_linear.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                   _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]
+        L.nvfp4_moe_workspace_size.restype = ctypes.c_size_t
+        L.nvfp4_moe_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
+        L.nvfp4_moe_grouped.restype = ctypes.c_int
+        L.nvfp4_moe_grouped.argtypes = [ctypes.POINTER(MoeArgs), _c_ptr]
+        if L.nvfp4_abi_version() != ABI_VERSION:
+            raise RuntimeError("libnvfp4.so ABI version does not match the binding")
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Nvfp4Error(status, lib().nvfp4_status_string(status).decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else _c_ptr(t.data_ptr())
+
+
+def _stream():
+    return _c_ptr(torch.cuda.current_stream().cuda_stream)
+
+
+def status_string(status: int) -> str:
+    return lib().nvfp4_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+
+
+def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
+                 out: Optional[Sequence[torch.Tensor]] = None):
+    """NVFP4-quantize bf16 activations [M, K].  ``gs`` None: the global scale is
+    computed on the device (max|x| / 2688) and returned; otherwise ``gs`` (a
+    1-element fp32 device tensor) is used.  Returns (codes [M,K/2] u8,
+    scales [M,K/16] u8, gs [1] fp32)."""
+    m, k = x.shape
+    if out is None:
+        q = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+        sf = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
+    else:
+        q, sf = out
+    compute = gs is None
+    gsb = torch.empty(1, dtype=torch.float32, device=x.device) if compute else gs
+    _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _stream()))
+    return q, sf, gsb
+
+
+def linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Optional[torch.Tensor] = None,
+           x_fp4: Optional[torch.Tensor] = None, x_sf: Optional[torch.Tensor] = None,
+           gsa: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[M, N] = x @ W^T (bf16 out).  Activations: ``x`` bf16 [M, K], or
+    ``x_fp4`` [M, K/2] + ``x_sf`` [M, K/16] + ``gsa`` [1]."""
+    n = w.shape[0]
+    k = w.shape[1] * 2
+    m = (x if x is not None else x_fp4).shape[0]
+    dev = w.device
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    need = lib().nvfp4_linear_workspace_size(m, n, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().nvfp4_linear(_p(x), _p(x_fp4), _p(x_sf), _p(gsa), _p(w), _p(w_sf), _p(ws2),
+                              m, n, k, _p(y), _p(workspace), wsb, _stream()))
+    return y
+
+
+def moe_workspace_size(t: int, h: int, i: int, e: int, topk: int, has_shared: bool, h_fp4: bool) -> int:
+    return int(lib().nvfp4_moe_workspace_size(t, h, i, e, topk, int(has_shared), int(h_fp4)))
+
+
+def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                w1: torch.Tensor, w1_sf: torch.Tensor, w1_ws2: torch.Tensor,
+                w2: torch.Tensor, w2_sf: torch.Tensor, w2_ws2: torch.Tensor,
+                x: Optional[torch.Tensor] = None,
+                x_fp4: Optional[torch.Tensor] = None, x_sf: Optional[torch.Tensor] = None,
+                a1_gs: Optional[torch.Tensor] = None,
+                shared: Optional[Sequence[torch.Tensor]] = None,
+                a2_gs: Optional[torch.Tensor] = None, a2_gs_out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                offsets_out: Optional[torch.Tensor] = None, perm_out: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stage_events: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """One MoE layer (see nvfp4_moe_grouped in include/nvfp4.h).
+    ``shared`` = (s1, s1_sf, s1_ws2, s2, s2_sf, s2_ws2) or None."""
+    e, two_i, h_half = w1.shape
+    h = h_half * 2
+    i = two_i // 2
+    t, topk = topk_ids.shape
+    dev = w1.device
+    y = out if out is not None else torch.empty((t, h), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_size(t, h, i, e, topk, shared is not None, a2_gs is not None),
+                                dtype=torch.uint8, device=dev)
+    a = MoeArgs()
+    a.T, a.H, a.I, a.E, a.topk = t, h, i, e, topk
+    a.x, a.x_fp4, a.x_sf, a.a1_gs = _p(x), _p(x_fp4), _p(x_sf), _p(a1_gs)
+    a.a2_gs, a.a2_gs_out = _p(a2_gs), _p(a2_gs_out)
+    a.topk_ids, a.topk_w = _p(topk_ids), _p(topk_w)
+    a.w1, a.w1_sf, a.w1_ws2 = _p(w1), _p(w1_sf), _p(w1_ws2)
+    a.w2, a.w2_sf, a.w2_ws2 = _p(w2), _p(w2_sf), _p(w2_ws2)
+    if shared is not None:
+        s1, s1_sf, s1_ws2, s2, s2_sf, s2_ws2 = shared
+        a.s1, a.s1_sf, a.s1_ws2 = _p(s1), _p(s1_sf), _p(s1_ws2)
+        a.s2, a.s2_sf, a.s2_ws2 = _p(s2), _p(s2_sf), _p(s2_ws2)
+    a.workspace = _p(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.offsets_out, a.perm_out = _p(offsets_out), _p(perm_out)
+    a.y = _p(y)
+    if stage_events is not None:
+        arr = (_c_ptr * len(stage_events))(*[_c_ptr(int(v)) for v in stage_events])
+        a.stage_events = ctypes.cast(arr, ctypes.POINTER(_c_ptr))
+    _check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream()))
+    return y

@@ -1,0 +1,192 @@
+/*
+ * nvfp4.h - C ABI of the MI355X (gfx950) NVFP4 block-scaled linear and
+ * Mixture-of-Experts grouped GEMM library (libnvfp4.so).
+ *
+ * What is computed.  The block-scaled GEMM
+ *     y = (x * scale_a * gsa) @ (w * scale_b * gsb)^T
+ * as stated on page "nvfp4-megamoe-kernel, commit 1121cd7 -
+ * single_shot_inference.py" (the note on the weight-dequant global scale):
+ * every operand element is an E2M1 value times its FP8-E4M3 block scale times
+ * one fp32 global scale per tensor.  For weights the global scale is
+ * weight_scale_2 (page "commit efe63ca - single_shot_inference.py", notes on
+ * weight_scale_2 and on input_scale).  For NVFP4 activations it is the
+ * activation global scale gs = amax / (6 * 448), used as it is, never
+ * inverted (page "commit 4c6464e - vllm", note on the activation global
+ * scale).  The product of the two global scales is applied exactly once.
+ *
+ * Formats (all entry points):
+ *   E2M1 ("fp4"): 2 codes per byte, element 2j in bits 0-3, 2j+1 in bits 4-7;
+ *                 values {0, .5, 1, 1.5, 2, 3, 4, 6} with sign bit 3.
+ *   E4M3FN block scale: one byte per 16 consecutive K elements of a row.
+ *   Weights [N, K/2] bytes + scales [N, K/16] bytes, K contiguous ("N-major",
+ *   page "commit efe63ca", note on the checkpoint layout; scales are not
+ *   transposed, same page, note on scale assembly).
+ *   bf16 tensors are row-major with the last dimension contiguous.
+ *   K is always the logical element count, not the packed byte count
+ *   (page "commit 4c6464e", note on K being the hidden size).
+ *
+ * Pointers are DEVICE pointers unless marked "host".  `stream` is a
+ * hipStream_t (NULL = the default stream).  Every call only enqueues work on
+ * `stream` and returns; it never synchronises, never allocates or frees, and
+ * keeps no state between calls (calls on different streams may run
+ * concurrently as long as their buffers do not overlap).  The caller owns
+ * every buffer.
+ *
+ * Constraints (checked on the host before any launch):
+ *   K and every reduction length % 256 == 0; output widths % 16 == 0;
+ *   device pointers 16-byte aligned (scale and gs pointers 4-byte aligned);
+ *   sizes positive and below 2^31 elements per dimension.
+ * Errors: a negative NVFP4_ERR_* code is returned and nothing is launched
+ * when a check fails; NVFP4_ERR_LAUNCH reports a HIP launch error.  Values
+ * inside device buffers (expert ids, NaN scales) are not checked on the host:
+ * an expert id outside [0, E) makes that (token, expert) pair contribute
+ * zero; it can never cause an out-of-bounds access.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = -1,      /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = -2,     /* a size is out of range or not a required multiple */
+  NVFP4_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
+  NVFP4_ERR_WORKSPACE = -4, /* workspace missing or smaller than the size function says */
+  NVFP4_ERR_LAUNCH = -5,    /* a kernel launch failed (hipGetLastError) */
+  NVFP4_ERR_ARG = -6        /* an incompatible combination of optional arguments */
+};
+
+/* Host: a static, human-readable description of a status code. */
+const char* nvfp4_status_string(int status);
+
+/* Host: ABI version of this header (incremented on incompatible changes). */
+int nvfp4_abi_version(void);
+#define NVFP4_ABI_VERSION 1
+
+/*
+ * nvfp4_quantize_act - quantize bf16 activations to NVFP4.
+ * Page "commit 4c6464e - vllm": the activation quantizer
+ * (quantize_activation_nvfp4, named in the note on the custom-op GEMM) and
+ * the activation global scale gs = amax / (6 * 448) (note on the activation
+ * global scale).  Per 16-element block of a row:
+ *     scale byte = RNE_E4M3(amax_blk / (6 * gs)), saturating at 448;
+ *     code       = RNE_E2M1(x * (1 / (E4M3(byte) * gs))), saturating at 6;
+ * each step one IEEE fp32 operation in that order (so the result is
+ * reproducible bit for bit); gs == 0 gives all-zero codes and scales.
+ *   x_bf16     [M, K] bf16 input.
+ *   gs         device fp32 scalar: output when compute_gs != 0 (written with
+ *              max|x| / 2688 computed on the device), input otherwise.
+ *   x_fp4      [M, K/2] output codes; x_sf [M, K/16] output scale bytes.
+ * Requires K % 16 == 0 (K % 256 == 0 if the result feeds nvfp4_linear or
+ * nvfp4_moe_grouped).
+ */
+int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int compute_gs,
+                       uint8_t* x_fp4, uint8_t* x_sf, void* stream);
+
+/*
+ * nvfp4_linear - dense NVFP4 linear, y[M, N] = x[M, K] @ W[N, K]^T, bf16 out,
+ * fp32 accumulation (page "commit 1121cd7", the GEMM statement in the note on
+ * the weight-dequant global scale; the NVFP4 linear layer of page
+ * "commit efe63ca", note on weight_scale_2).
+ *   Activations, one of:
+ *     x_bf16 [M, K] bf16 (then x_fp4, x_sf, gsa must be NULL; scale_a = gsa = 1), or
+ *     x_fp4 [M, K/2] + x_sf [M, K/16] + gsa (device fp32 scalar) from nvfp4_quantize_act.
+ *   w_fp4 [N, K/2], w_sf [N, K/16]; gsb = device fp32 scalar weight_scale_2.
+ *   y_bf16 [M, N] bf16 output, fully overwritten.
+ *   workspace: device scratch of nvfp4_linear_workspace_size(M, N, K) bytes
+ *   (may be NULL when that size is 0).  Its contents are undefined after the
+ *   call; it must not be shared with a concurrently running call.
+ */
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
+                 const uint8_t* w_fp4, const uint8_t* w_sf, const float* gsb,
+                 int64_t M, int64_t N, int64_t K, void* y_bf16,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_moe_grouped - one Mixture-of-Experts layer with NVFP4 experts.
+ * Routed experts (stacked (E, N, K), page "commit efe63ca", note on stacking
+ * experts; one weight_scale_2 per expert and layer, same page, note on
+ * weight_scale_2) and an optional shared expert (Nvfp4SharedExpert, same
+ * note).  For every token t and routed slot j, with e = topk_ids[t, j]:
+ *     gate|up = x_t @ W1_e^T          (W1 rows [0, I) = gate, [I, 2I) = up)
+ *     h       = silu(gate) * up        (silu(z) = z / (1 + e^-z))
+ *     o       = h @ W2_e^T
+ *     y_t     = sum_{j=0..topk-1} topk_w[t, j] * o(t, j)  +  o_shared(t)
+ * computed as: a stable token->expert permutation with int32 segment offsets
+ * (page "commit 4c6464e", note on the custom-op GEMM: int32 expert offsets),
+ * a grouped gate/up GEMM with a fused SwiGLU epilogue, a grouped down GEMM
+ * that scatters each pair's output row, and a weighted combine in the fixed
+ * order j = 0..topk-1 then the shared expert.
+ *
+ * Activations, one of:
+ *   x [T, H] bf16                          (x_fp4, x_sf, a1_gs NULL), or
+ *   x_fp4 [T, H/2] + x_sf [T, H/16] + a1_gs (from nvfp4_quantize_act).
+ * Hidden activations h:
+ *   a2_gs != NULL: h is quantized to NVFP4 with global scale *a2_gs (the
+ *                  nvfp4_quantize_act rule with a supplied gs) and the down
+ *                  GEMM runs on NVFP4 activations (fully-FP4 path);
+ *   a2_gs == NULL: h stays fp32.  If a2_gs_out != NULL it receives
+ *                  max|h| / 2688, the calibrated global scale of h for later
+ *                  calls (the warm-up calibration of page "commit 4c6464e").
+ * Weights: w1 [E, 2I, H/2], w1_sf [E, 2I, H/16], w1_ws2 [E] fp32;
+ *          w2 [E, H, I/2],  w2_sf [E, H, I/16],  w2_ws2 [E] fp32;
+ *          shared expert s1/s1_sf/s1_ws2[1], s2/s2_sf/s2_ws2[1], all NULL if absent.
+ * Routing: topk_ids [T, topk] int32 (distinct ids per token expected),
+ *          topk_w [T, topk] fp32 combine weights (applied after the down GEMM).
+ * Optional outputs: offsets_out [E + 2] int32 (group starts; offsets_out[E] =
+ *          number of routed rows, offsets_out[E+1] = that + T if shared),
+ *          perm_out [T*topk + T] int32 (sorted row -> pair id t*topk + j;
+ *          shared rows hold T*topk + t).
+ * y [T, H] bf16 output, fully overwritten.
+ * workspace: nvfp4_moe_workspace_size(...) bytes of device scratch; h_fp4 = 1
+ * sizes it for calls with a2_gs != NULL (smaller), 0 for a2_gs == NULL.
+ * stage_events: optional host array of 5 hipEvent_t; event i is recorded on
+ * `stream` before stage i (permute, gate/up GEMM, down GEMM, combine) and
+ * event 4 after the last one (instrumentation for timing single kernels).
+ */
+typedef struct nvfp4_moe_args {
+  int64_t T, H, I, E, topk;
+  const void* x;
+  const uint8_t* x_fp4;
+  const uint8_t* x_sf;
+  const float* a1_gs;
+  const float* a2_gs;
+  float* a2_gs_out;
+  const int32_t* topk_ids;
+  const float* topk_w;
+  const uint8_t* w1;
+  const uint8_t* w1_sf;
+  const float* w1_ws2;
+  const uint8_t* w2;
+  const uint8_t* w2_sf;
+  const float* w2_ws2;
+  const uint8_t* s1;
+  const uint8_t* s1_sf;
+  const float* s1_ws2;
+  const uint8_t* s2;
+  const uint8_t* s2_sf;
+  const float* s2_ws2;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* offsets_out;
+  int32_t* perm_out;
+  void* y;
+  void** stage_events;
+} nvfp4_moe_args;
+
+size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                                int has_shared, int h_fp4);
+int nvfp4_moe_grouped(const nvfp4_moe_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

@@ -1,0 +1,103 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and host-side validation returns the documented status codes
+before anything is launched (no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_block_scaled_route_amd import ops
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("libnvfp4.so not built")
+    return ops.lib()
+
+
+def test_header_declares_the_binding_entry_points():
+    assert _declared() == sorted(ops.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == ops.ABI_VERSION
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.nvfp4_status_string(code)
+    assert lib.nvfp4_status_string(-99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_linear_validation(lib):
+    L = lib
+    args = lambda **kw: dict(dict(x=FAKE, xq=None, xs=None, gsa=None, w=FAKE, ws=FAKE, gsb=FAKE,  # noqa: E731
+                                  M=8, N=128, K=256, y=FAKE, work=FAKE, wb=1 << 20), **kw)
+
+    def call(a):
+        return L.nvfp4_linear(a["x"], a["xq"], a["xs"], a["gsa"], a["w"], a["ws"], a["gsb"],
+                              a["M"], a["N"], a["K"], a["y"], a["work"], a["wb"], None)
+    assert call(args(K=200)) == -2          # K not a multiple of 256
+    assert call(args(N=100)) == -2          # N not a multiple of 16
+    assert call(args(M=-1)) == -2
+    assert call(args(M=0)) == 0             # nothing to do, nothing launched
+    assert call(args(w=None)) == -1
+    assert call(args(x=None)) == -1
+    assert call(args(xq=FAKE)) == -6        # both activation forms
+    assert call(args(y=ctypes.c_void_p(0x1004))) == -3
+    assert call(args(work=None)) == -4
+    assert call(args(wb=4)) == -4
+
+
+def test_quantize_validation(lib):
+    L = lib
+    assert L.nvfp4_quantize_act(FAKE, 4, 40, FAKE, 1, FAKE, FAKE, None) == -2
+    assert L.nvfp4_quantize_act(FAKE, 4, 64, None, 1, FAKE, FAKE, None) == -1
+    assert L.nvfp4_quantize_act(None, 4, 64, FAKE, 1, FAKE, FAKE, None) == -1
+    assert L.nvfp4_quantize_act(ctypes.c_void_p(0x1002), 4, 64, FAKE, 1, FAKE, FAKE, None) == -3
+
+
+def test_moe_validation(lib):
+    L = lib
+    ws_shared = L.nvfp4_moe_workspace_size(64, 7168, 2048, 384, 8, 1, 0)
+    ws = L.nvfp4_moe_workspace_size(64, 7168, 2048, 384, 8, 0, 0)      # no shared expert, fp32 h
+    ws4 = L.nvfp4_moe_workspace_size(64, 7168, 2048, 384, 8, 0, 1)     # NVFP4 h
+    assert ws_shared > ws > ws4 > 0
+
+    def base(**kw):
+        a = ops.MoeArgs()
+        a.T, a.H, a.I, a.E, a.topk = 64, 7168, 2048, 384, 8
+        for f in ("x", "topk_ids", "topk_w", "w1", "w1_sf", "w1_ws2", "w2", "w2_sf", "w2_ws2", "y", "workspace"):
+            setattr(a, f, FAKE)
+        a.workspace_bytes = ws
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return L.nvfp4_moe_grouped(ctypes.byref(a), None)
+    assert base(H=7000) == -2
+    assert base(I=100) == -2
+    assert base(E=1000) == -2               # more experts than the permutation supports
+    assert base(topk=400) == -2
+    assert base(T=0) == 0
+    assert base(w1=None) == -1
+    assert base(x=None) == -1
+    assert base(x_fp4=FAKE, x_sf=FAKE, a1_gs=FAKE) == -6     # both activation forms
+    assert base(s1=FAKE) == -1                                # half a shared expert
+    assert base(s2=FAKE) == -6
+    assert base(a2_gs=FAKE, a2_gs_out=FAKE) == -6
+    assert base(workspace_bytes=ws - 1) == -4
+    assert base(y=ctypes.c_void_p(0x1008)) == -3

@@ -1,0 +1,87 @@
+"""GPU parity of nvfp4_linear against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import compare, dev, f32, say
+from fp4_block_scaled_route_amd import ops, synth
+from oracle import linear, quant
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_bf16(li):
+    return ops.linear(dev(li.w), dev(li.w_sf), f32(li.ws2), x=dev(li.x))
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (8, 128, 256),                                      # single NVFP4 linear, seed 0
+    (1, 1536, 7168), (32, 1536, 7168), (128, 1536, 7168),   # projection shape
+    (1, 24576, 1536), (32, 24576, 1536), (128, 24576, 1536),
+    (17, 48, 512), (100, 64, 256), (129, 32, 768),      # ragged token counts (several passes)
+])
+def test_linear_bf16(m, n, k):
+    say(f"linear bf16 M={m} N={n} K={k}")
+    li = synth.make_linear(m, n, k, seed=0)
+    y = _run_bf16(li)
+    torch.cuda.synchronize()
+    ref = linear.linear_bf16(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
+    compare(y, ref, what=f"linear {m}x{n}x{k}")
+
+
+def test_linear_hand_worked_golden():
+    from conftest import golden_dict
+    g = golden_dict("linear_example.txt")
+    # the fixture has K=16; pad K to 256 with zero codes (K must be a multiple of 256)
+    w = np.zeros((16, 128), np.uint8)
+    sf = np.zeros((16, 16), np.uint8)
+    w[0, :8] = [int(b, 16) for b in g["w_row0"]]
+    w[1, :8] = [int(b, 16) for b in g["w_row1"]]
+    sf[0, 0] = int(g["sf"][0], 16)
+    sf[1, 0] = int(g["sf"][1], 16)
+    x = np.zeros((2, 256), np.float32)
+    x[0, :16] = [float(v) for v in g["x_row0"]]
+    x[1, :16] = [float(v) for v in g["x_row1"]]
+    y = ops.linear(dev(w), dev(sf), f32(float(g["ws2"][0])), x=dev(torch.from_numpy(x).to(torch.bfloat16)))
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    assert y[0, 0] == 12 and y[0, 1] == -13 and y[1, 0] == -0.5 and y[1, 1] == -1.375
+    assert not y[:, 2:].any()
+
+
+def test_linear_extreme_activation_range():
+    """bf16 activations far outside fp16's range are staged exactly (per-row
+    power-of-two shift)."""
+    li = synth.make_linear(4, 64, 512, seed=2)
+    x = li.x.float()
+    x[0] *= 2.0 ** 100
+    x[1] *= 2.0 ** -100
+    x[2, :] = 0
+    li.x = x.to(torch.bfloat16)
+    y = _run_bf16(li)
+    torch.cuda.synchronize()
+    ref = linear.linear_bf16(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
+    for r in (0, 1, 3):
+        compare(y[r:r + 1], ref[r:r + 1], what=f"row {r}")
+    assert not y[2].float().abs().sum()
+
+
+@pytest.mark.parametrize("m,n,k", [(8, 128, 256), (128, 1536, 7168), (33, 256, 1536)])
+def test_linear_nvfp4_activations(m, n, k):
+    say(f"linear nvfp4 M={m} N={n} K={k}")
+    li = synth.make_linear(m, n, k, seed=1)
+    xq, xs, gs = ops.quantize_act(dev(li.x))
+    y = ops.linear(dev(li.w), dev(li.w_sf), f32(li.ws2), x_fp4=xq, x_sf=xs, gsa=gs)
+    torch.cuda.synchronize()
+    rq, rs, rgs = quant.quantize_nvfp4(li.x.float().numpy())
+    ref = linear.linear_nvfp4(rq, rs, rgs, li.w, li.w_sf, li.ws2)
+    compare(y, ref, what="nvfp4 x nvfp4")
+
+
+def test_linear_empty_and_errors():
+    li = synth.make_linear(1, 16, 256, seed=0)
+    y = ops.linear(dev(li.w), dev(li.w_sf), f32(li.ws2), x=dev(li.x[:0]))
+    assert y.shape == (0, 16)
+    with pytest.raises(ops.Nvfp4Error) as e:
+        ops.linear(dev(li.w[:, :100]), dev(li.w_sf[:, :12]), f32(li.ws2), x=dev(li.x[:, :200]))
+    assert e.value.status == -2

@@ -1,0 +1,189 @@
+"""GPU parity of nvfp4_moe_grouped against the oracle.
+
+Small shapes are compared in full; the DeepSeek-V4-shaped configurations
+(hidden 7168, intermediate 2048, 384 experts, top-8) run on the GPU at full
+size in the launch configuration the benchmark times, and are compared on
+sampled tokens (the oracle computes those one expert at a time).  The
+permutation (segment offsets and sorted-row order) is compared bit for bit
+at every size."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DeviceExperts, compare, dev, f32, full_size_experts, say
+from fp4_block_scaled_route_amd import ops, synth
+from oracle import codec, moe, quant
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(de, ids, w, x=None, shared=None, x_fp4=None, x_sf=None, a1_gs=None, a2_gs=None, a2_gs_out=None):
+    t, k = ids.shape
+    e = de.w1.shape[0]
+    off = torch.empty(e + 2, dtype=torch.int32, device="cuda")
+    perm = torch.empty(t * k + t, dtype=torch.int32, device="cuda")
+    y = ops.moe_grouped(dev(ids), dev(w), **de.args(), x=x, x_fp4=x_fp4, x_sf=x_sf, a1_gs=a1_gs,
+                        shared=shared.as_shared() if shared is not None else None,
+                        a2_gs=a2_gs, a2_gs_out=a2_gs_out, offsets_out=off, perm_out=perm)
+    torch.cuda.synchronize()
+    return y, off.cpu().numpy(), perm.cpu().numpy()
+
+
+def _check_perm(ids, e, has_shared, off, perm):
+    ro, rp, _ = moe.permute(ids, e, has_shared)
+    assert np.array_equal(off, ro), "segment offsets differ"
+    n = ro[-1]
+    assert np.array_equal(perm[:n], rp), "sorted-row order differs"
+
+
+def _oracle(x_rows, ids, w, host, shared_host, tokens, a2_gs=None):
+    return moe.moe_forward(x_rows, ids, w, host.expert,
+                           shared_host.expert(0) if shared_host is not None else None,
+                           a2_gs=a2_gs, tokens=tokens)
+
+
+@pytest.mark.parametrize("t,h,i,e,k,routing,shared", [
+    (37, 512, 256, 16, 4, "uniform", True),
+    (64, 256, 512, 8, 2, "zipf", False),
+    (1, 256, 256, 4, 4, "uniform", True),
+    (300, 256, 256, 6, 3, "zipf", True),     # hot groups with > 128 rows: several passes
+])
+def test_moe_small_bf16(t, h, i, e, k, routing, shared):
+    say(f"moe bf16 T={t} H={h} I={i} E={e} k={k} {routing} shared={shared}")
+    mi = synth.make_moe(t, h, i, e, k, seed=4, routing=routing, shared=shared, threads=4)
+    de = DeviceExperts(mi.experts)
+    ds = DeviceExperts(mi.shared) if shared else None
+    y, off, perm = _run(de, mi.topk_ids, mi.topk_w, x=dev(mi.x), shared=ds)
+    _check_perm(mi.topk_ids, e, shared, off, perm)
+    ref = _oracle(synth.bf16_to_float64(mi.x), mi.topk_ids, mi.topk_w, mi.experts, mi.shared, None)
+    compare(y, ref, what="moe small")
+
+
+def test_moe_identical_experts_invariant():
+    """All experts (and the shared one) identical: y = (sum_j w + 1) * FFN(x)
+    whatever the routing; checks weights and combine without indexing."""
+    t, h, i, e, k = 20, 256, 256, 6, 3
+    mi = synth.make_moe(t, h, i, e, k, seed=5, shared=True, threads=2)
+    one = synth.make_experts(1, h, i, seed=9)
+    same = synth.ExpertSet(*(np.repeat(a, e, axis=0) for a in
+                             (one.w1, one.w1_sf, one.w1_ws2, one.w2, one.w2_sf, one.w2_ws2)))
+    y, _, _ = _run(DeviceExperts(same), mi.topk_ids, mi.topk_w, x=dev(mi.x), shared=DeviceExperts(one))
+    x = synth.bf16_to_float64(mi.x)
+    ex = one.expert(0)
+    f = moe.expert_ffn(x, codec.dequant_nvfp4(*ex[:3]), codec.dequant_nvfp4(*ex[3:]))
+    ref = (mi.topk_w.astype(np.float64).sum(1) + 1.0)[:, None] * f
+    compare(y, ref, what="identical experts")
+
+
+def test_moe_out_of_range_ids_contribute_nothing():
+    t, h, i, e, k = 8, 256, 256, 4, 2
+    mi = synth.make_moe(t, h, i, e, k, seed=6, shared=False, threads=2)
+    ids = mi.topk_ids.copy()
+    ids[2, 1] = e + 3
+    ids[5, 0] = -1
+    de = DeviceExperts(mi.experts)
+    y, _, _ = _run(de, ids, mi.topk_w, x=dev(mi.x))
+    w = mi.topk_w.copy()
+    w[2, 1] = 0
+    w[5, 0] = 0
+    ids_ok = ids.copy()
+    ids_ok[2, 1] = 0
+    ids_ok[5, 0] = 0
+    ref = _oracle(synth.bf16_to_float64(mi.x), ids_ok, w, mi.experts, None, None)
+    compare(y, ref, what="invalid ids")
+
+
+def test_moe_small_fully_fp4_and_calibration():
+    t, h, i, e, k = 40, 512, 512, 8, 4
+    say("moe fully fp4 small")
+    mi = synth.make_moe(t, h, i, e, k, seed=7, shared=True, threads=2)
+    de, ds = DeviceExperts(mi.experts), DeviceExperts(mi.shared)
+    # calibration call (h kept fp32): a2_gs_out = max|h| / 2688
+    xq, xs, gs = ops.quantize_act(dev(mi.x))
+    gs_out = f32(0)
+    _run(de, mi.topk_ids, mi.topk_w, x_fp4=xq, x_sf=xs, a1_gs=gs, shared=ds, a2_gs_out=gs_out)
+    rq, rs, rgs = quant.quantize_nvfp4(mi.x.float().numpy())
+    xa = quant.dequantize_nvfp4(rq, rs, rgs)
+    amax = 0.0
+    for tt in range(t):
+        for j in range(k):
+            ex = mi.experts.expert(int(mi.topk_ids[tt, j]))
+            amax = max(amax, moe.hidden_amax(xa[tt:tt + 1], codec.dequant_nvfp4(*ex[:3])))
+        amax = max(amax, moe.hidden_amax(xa[tt:tt + 1], codec.dequant_nvfp4(*mi.shared.expert(0)[:3])))
+    a2 = np.float32(np.float32(amax) / np.float32(2688.0))
+    assert abs(gs_out.item() - a2) <= 1e-4 * a2, (gs_out.item(), a2)
+    # fully FP4 call with the oracle's calibrated scale
+    y, off, perm = _run(de, mi.topk_ids, mi.topk_w, x_fp4=xq, x_sf=xs, a1_gs=gs, shared=ds, a2_gs=f32(a2))
+    _check_perm(mi.topk_ids, e, True, off, perm)
+    ref = _oracle(xa, mi.topk_ids, mi.topk_w, mi.experts, mi.shared, None, a2_gs=a2)
+    compare(y, ref, what="fully fp4 small")
+
+
+# ---------------------------------------------------------------------------
+# full DeepSeek-V4-shaped configurations, sampled tokens
+# ---------------------------------------------------------------------------
+
+
+def _sampled(t, rng, extra=()):
+    return sorted(set(int(v) for v in rng.choice(t, size=3, replace=False)) | set(extra))
+
+
+def test_moe_decode_step_full_size():
+    """MoE decode step: 64 tokens, hidden 7168, 384 experts top-8 softmax
+    routing from N(0,1) logits, W1 [4096, 7168], W2 [7168, 2048], shared expert."""
+    say("moe decode step full size")
+    de, ds = full_size_experts()
+    t, e, k = 64, 384, 8
+    x = synth.bf16_normal((t, 7168), 0)
+    ids, w = synth.route(t, e, k, seed=0, mode="uniform")
+    y, off, perm = _run(de, ids, w, x=dev(x), shared=ds)
+    _check_perm(ids, e, True, off, perm)
+    toks = _sampled(t, np.random.default_rng(0), extra=(0, t - 1))
+    ref = _oracle(synth.bf16_to_float64(x), ids, w, de.host, ds.host, toks)
+    compare(y[toks], ref, what="decode sampled")
+
+
+def test_moe_prefill_chunk_full_size():
+    """MoE prefill chunk: 128 tokens, Zipf(1.1)-skewed routing, shared expert."""
+    say("moe prefill chunk full size")
+    de, ds = full_size_experts()
+    t, e, k = 128, 384, 8
+    x = synth.bf16_normal((t, 7168), 1)
+    ids, w = synth.route(t, e, k, seed=1, mode="zipf", zipf_s=1.1)
+    y, off, perm = _run(de, ids, w, x=dev(x), shared=ds)
+    _check_perm(ids, e, True, off, perm)
+    hot = int(np.bincount(ids.ravel(), minlength=e).argmax())
+    hot_tok = int(np.nonzero((ids == hot).any(1))[0][0])
+    toks = _sampled(t, np.random.default_rng(1), extra=(hot_tok,))
+    ref = _oracle(synth.bf16_to_float64(x), ids, w, de.host, ds.host, toks)
+    compare(y[toks], ref, what="prefill sampled")
+
+
+def test_moe_fully_fp4_large_batch_full_size():
+    """Fully FP4 path: 4096 tokens quantized with gs = amax/(6*448), uniform
+    top-8 routing, both GEMMs on NVFP4 activations, no shared expert."""
+    say("moe fully fp4 4096 tokens full size")
+    de, _ = full_size_experts()
+    t, e, k = 4096, 384, 8
+    x = synth.bf16_normal((t, 7168), 2)
+    ids, w = synth.route(t, e, k, seed=2, mode="uniform")
+    xq, xs, gs = ops.quantize_act(dev(x))
+    rq, rs, rgs = quant.quantize_nvfp4(x.float().numpy())
+    torch.cuda.synchronize()
+    assert gs.item() == float(rgs)
+    assert np.array_equal(xs.cpu().numpy(), rs) and np.array_equal(xq.cpu().numpy(), rq)
+    toks = _sampled(t, np.random.default_rng(2), extra=(0,))
+    xa = quant.dequantize_nvfp4(rq[toks], rs[toks], rgs)
+    xa_full = np.zeros((t, 7168))
+    xa_full[toks] = xa
+    # warm-up calibration of h's global scale on the sampled tokens (oracle side)
+    amax = 0.0
+    for tt in toks:
+        for j in range(k):
+            ex = de.host.expert(int(ids[tt, j]))
+            amax = max(amax, moe.hidden_amax(xa_full[tt:tt + 1], codec.dequant_nvfp4(*ex[:3])))
+    a2 = np.float32(np.float32(amax) / np.float32(2688.0))
+    y, off, perm = _run(de, ids, w, x_fp4=xq, x_sf=xs, a1_gs=gs, a2_gs=f32(a2))
+    _check_perm(ids, e, False, off, perm)
+    ref = _oracle(xa_full, ids, w, de.host, None, toks, a2_gs=a2)
+    compare(y[toks], ref, what="fully fp4 sampled")
