@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 MoE layer (and dense linear) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input that is already resident in HBM: for the MoE workloads one
+nvfp4_moe_grouped call (permute, gate/up GEMM + SwiGLU, down GEMM + scatter,
+weighted combine), preceded by nvfp4_quantize_act on the fully-FP4 workload.
+Prints ONE JSON line.  `value` is the step's algorithmic HBM throughput
+(bytes of every touched expert's NVFP4 weights and scales + activations in +
+output out, per second); TFLOP/s is reported beside it.  The roofline object
+describes the dominant kernel (the gate/up GEMM), timed with HIP events
+recorded around it on the stream it runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+BYTES_PER_EXPERT_W1 = 2 * 2048 * 7168 // 2 + 2 * 2048 * 7168 // 16       # 16,515,072
+BYTES_PER_EXPERT_W2 = 7168 * 2048 // 2 + 7168 * 2048 // 16               # 8,257,536
+FLOPS_PER_PAIR = 2 * (2 * 2048 * 7168 + 7168 * 2048)                     # 88,080,384
+
+WORKLOADS = {
+    # MoE decode step: 64 tokens, 384 experts, top-8 softmax routing, shared expert
+    "moe_decode": dict(kind="moe", T=64, H=7168, I=2048, E=384, k=8, routing="uniform", shared=True, fp4=False),
+    # MoE prefill chunk: 128 tokens, Zipf(1.1) routing, shared expert
+    "moe_prefill": dict(kind="moe", T=128, H=7168, I=2048, E=384, k=8, routing="zipf", shared=True, fp4=False),
+    # fully FP4 path: 4096 tokens, both GEMMs on NVFP4 activations, no shared expert
+    "moe_fp4": dict(kind="moe", T=4096, H=7168, I=2048, E=384, k=8, routing="uniform", shared=False, fp4=True),
+    # dense NVFP4 linear at projection shapes
+    "linear_q_a_m1": dict(kind="linear", M=1, N=1536, K=7168),
+    "linear_q_a_m128": dict(kind="linear", M=128, N=1536, K=7168),
+    "linear_q_b_m128": dict(kind="linear", M=128, N=24576, K=1536),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the stream its
+    kernels run on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(ev.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_block_scaled_route_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, src_hash):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_swiglu_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# MoE workload
+# ---------------------------------------------------------------------------
+
+
+def setup_moe(cfg, seed):
+    import numpy as np
+    import torch
+
+    from fp4_block_scaled_route_amd import ops, synth
+
+    t0 = time.time()
+    mi = synth.make_moe(cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"], seed=seed, routing=cfg["routing"],
+                        shared=cfg["shared"])
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    ex = mi.experts
+    dev = dict(topk_ids=d(mi.topk_ids), topk_w=d(mi.topk_w), w1=d(ex.w1), w1_sf=d(ex.w1_sf),
+               w1_ws2=d(ex.w1_ws2), w2=d(ex.w2), w2_sf=d(ex.w2_sf), w2_ws2=d(ex.w2_ws2))
+    shared = None
+    if mi.shared is not None:
+        s = mi.shared
+        shared = (d(s.w1[0]), d(s.w1_sf[0]), d(s.w1_ws2), d(s.w2[0]), d(s.w2_sf[0]), d(s.w2_ws2))
+    x = mi.x.cuda()
+    t, k, h, i, e = cfg["T"], cfg["k"], cfg["H"], cfg["I"], cfg["E"]
+    ws = torch.empty(ops.moe_workspace_size(t, h, i, e, k, shared is not None, cfg["fp4"]),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
+    state = dict(mi=mi, dev=dev, shared=shared, x=x, ws=ws, y=y)
+    if cfg["fp4"]:
+        # warm-up calibration of the hidden activations' global scale (h kept
+        # fp32 for this one call, a2_gs_out = max|h| / 2688)
+        xq, xs, gs = ops.quantize_act(x)
+        a2 = torch.zeros(1, dtype=torch.float32, device="cuda")
+        ws_cal = torch.empty(ops.moe_workspace_size(t, h, i, e, k, shared is not None, False),
+                             dtype=torch.uint8, device="cuda")
+        ops.moe_grouped(**dev, x_fp4=xq, x_sf=xs, a1_gs=gs, shared=shared, a2_gs_out=a2, workspace=ws_cal, out=y)
+        torch.cuda.synchronize()
+        del ws_cal
+        state.update(xq=xq, xs=xs, gs=gs, a2=a2)
+        log(f"calibrated a2_gs = {a2.item():.6g}")
+    torch.cuda.synchronize()
+    return state
+
+
+def moe_step(cfg, st, events=None):
+    from fp4_block_scaled_route_amd import ops
+    if cfg["fp4"]:
+        xq, xs, gs = ops.quantize_act(st["x"], out=(st["xq"], st["xs"]), gs_out=st["gs"])
+        return ops.moe_grouped(**st["dev"], x_fp4=xq, x_sf=xs, a1_gs=gs, shared=st["shared"], a2_gs=st["a2"],
+                               workspace=st["ws"], out=st["y"], stage_events=events)
+    return ops.moe_grouped(**st["dev"], x=st["x"], shared=st["shared"], workspace=st["ws"], out=st["y"],
+                           stage_events=events)
+
+
+def moe_accounting(cfg, st):
+    import numpy as np
+    ids = st["mi"].topk_ids
+    touched = int(np.unique(ids).size)
+    S = 1 if cfg["shared"] else 0
+    t, h = cfg["T"], cfg["H"]
+    pairs = t * cfg["k"] + S * t
+    flops = pairs * FLOPS_PER_PAIR
+    act_in = t * h * 2                                   # bf16 x (the fully-FP4 step reads x too: it quantizes it)
+    if cfg["fp4"]:
+        act_in += t * (h // 2 + h // 16) * 2             # x_fp4 + scales written, then read by the GEMM
+    out = t * h * 2
+    w_bytes = (touched + S) * (BYTES_PER_EXPERT_W1 + BYTES_PER_EXPERT_W2)
+    step_bytes = w_bytes + act_in + out
+    # gate/up GEMM: W1 + scales of every touched expert, activations read once
+    g1_bytes = (touched + S) * BYTES_PER_EXPERT_W1 + (t * (h // 2 + h // 16) if cfg["fp4"] else t * h * 2)
+    g1_flops = pairs * 2 * (2 * 2048 * 7168)
+    return dict(touched=touched, flops=flops, step_bytes=step_bytes, g1_bytes=g1_bytes, g1_flops=g1_flops)
+
+
+def moe_cpu_baseline(cfg, st, budget_s=20.0):
+    """The oracle, timed on the host on a bounded sample of the same workload:
+    the first few tokens of the batch, computed in full (all their experts)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from fp4_block_scaled_route_amd import synth
+    from oracle import moe, quant
+
+    mi = st["mi"]
+    x = synth.bf16_to_float64(mi.x)
+    ntok = 2
+    toks = list(range(ntok))
+    if cfg["fp4"]:
+        rq, rs, rgs = quant.quantize_nvfp4(mi.x[:ntok].float().numpy(), gs=np.float32(st["gs"].item()))
+        x = np.zeros_like(x[:ntok])
+        x[:] = quant.dequantize_nvfp4(rq, rs, rgs)
+    t0 = time.perf_counter()
+    shared = mi.shared.expert(0) if mi.shared is not None else None
+    moe.moe_forward(x, mi.topk_ids[:ntok], mi.topk_w[:ntok], mi.experts.expert, shared,
+                    a2_gs=(np.float32(st["a2"].item()) if cfg["fp4"] else None), tokens=toks)
+    dt = time.perf_counter() - t0
+    touched = int(np.unique(mi.topk_ids[:ntok]).size) + (1 if shared is not None else 0)
+    nbytes = touched * (BYTES_PER_EXPERT_W1 + BYTES_PER_EXPERT_W2) + ntok * cfg["H"] * 4
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"first {ntok} tokens of the batch, all {touched} experts they touch, "
+                       f"float64 numpy oracle, {dt:.1f}s wall",
+                seconds=round(dt, 2))
+
+
+def run_moe(args, cfg):
+    import torch
+    st = setup_moe(cfg, args.seed)
+    acc = moe_accounting(cfg, st)
+    for _ in range(args.warmup):
+        moe_step(cfg, st)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    evs = [hip.create(5) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        moe_step(cfg, st, events=evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    stage = [0.0] * 4
+    for s in range(args.steps):
+        for i in range(4):
+            stage[i] += hip.elapsed_ms(evs[s][i], evs[s][i + 1]) / args.steps
+    for e in evs:
+        hip.destroy(e)
+    g1_ms = stage[1]
+    src = kernel_source_hash()
+    traffic = read_traffic(args.workload, src)
+    gbs = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
+    tflops = acc["flops"] / (ms_step * 1e-3) / 1e12
+    if cfg["fp4"]:
+        g1_tflops = acc["g1_flops"] / (g1_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(g1_tflops, 2), peak=FP16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(g1_tflops / FP16_PEAK_TFLOPS, 4), traffic=traffic)
+    else:
+        g1_gbs = acc["g1_bytes"] / (g1_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(g1_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(g1_gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+    roof.update(kernel="nvfp4_grouped_gemm (gate/up + SwiGLU)", kernel_ms=round(g1_ms, 4),
+                algorithmic_bytes_per_launch=acc["g1_bytes"], algorithmic_flops_per_launch=acc["g1_flops"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = moe_cpu_baseline(cfg, st)
+    name = {"moe_decode": "MoE decode step", "moe_prefill": "MoE prefill chunk",
+            "moe_fp4": "fully FP4 MoE at large batch"}[args.workload]
+    result = {
+        "metric": "NVFP4 MoE grouped-GEMM TFLOP/s + HBM GB/s (%roofline), 1xMI355X",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {cfg['T']} tokens x hidden {cfg['H']}, {cfg['E']} experts top-{cfg['k']} "
+                               f"({cfg['routing']} routing), W1 [4096,7168] W2 [7168,2048] NVFP4"
+                               f"{', shared expert' if cfg['shared'] else ''}"
+                               f"{', NVFP4 activations' if cfg['fp4'] else ', bf16 activations'}",
+                   "name": args.workload, "tokens": cfg["T"], "touched_experts": acc["touched"],
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": acc["step_bytes"],
+        "algorithmic_flops_per_step": acc["flops"],
+        "stage_ms": {"permute": round(stage[0], 4), "gate_up_swiglu": round(stage[1], 4),
+                     "down_scatter": round(stage[2], 4), "combine": round(stage[3], 4)},
+        "wall_s": round(t_wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src,
+    }
+    return result
+
+
+# ---------------------------------------------------------------------------
+# dense linear workload
+# ---------------------------------------------------------------------------
+
+
+def run_linear(args, cfg):
+    import numpy as np
+    import torch
+
+    from fp4_block_scaled_route_amd import ops, synth
+
+    m, n, k = cfg["M"], cfg["N"], cfg["K"]
+    li = synth.make_linear(m, n, k, seed=args.seed)
+    w_bytes = n * (k // 2 + k // 16)
+    # rotate copies of W so that the working set exceeds the 256 MB last-level cache
+    copies = max(1, int(np.ceil(1.0e9 / w_bytes)))
+    ws = [torch.from_numpy(li.w).cuda() for _ in range(copies)]
+    sfs = [torch.from_numpy(li.w_sf).cuda() for _ in range(copies)]
+    ws2 = torch.tensor([li.ws2], dtype=torch.float32, device="cuda")
+    x = li.x.cuda()
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    work = torch.empty(max(1, ops.lib().nvfp4_linear_workspace_size(m, n, k)), dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        ops.linear(ws[i % copies], sfs[i % copies], ws2, x=x, out=y, workspace=work)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        ops.linear(ws[i % copies], sfs[i % copies], ws2, x=x, out=y, workspace=work)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = w_bytes + m * k * 2 + m * n * 2
+    flops = 2 * m * n * k
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "NVFP4 linear HBM GB/s (%roofline), 1xMI355X", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"dense NVFP4 linear x[{m},{k}] @ W[{n},{k}]^T, bf16 out, {copies} rotating "
+                               f"weight copies", "name": args.workload},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None),
+        "cpu_baseline": None,
+    }
+
+
+def run_copy(args):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings to bytes."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="moe_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
+              "mode: the sharding design is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        run_copy(args)
+        return
+    cfg = WORKLOADS[args.workload]
+    res = run_moe(args, cfg) if cfg["kind"] == "moe" else run_linear(args, cfg)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

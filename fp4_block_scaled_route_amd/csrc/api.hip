@@ -11,6 +11,7 @@ using namespace nvfp4;
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxBuffer = (int64_t)1 << 32;
 constexpr int kMaxExperts = 512;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -20,7 +21,6 @@ int launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_
 // Number of 16-row activation chunks a group pass holds, from the expected rows per group.
 int pick_maxc(double rows_per_group) {
   const double want = rows_per_group * 1.25 / 16.0;
-  if (want <= 1.0) return 1;
   if (want <= 2.0) return 2;
   if (want <= 4.0) return 4;
   return 8;
@@ -28,7 +28,7 @@ int pick_maxc(double rows_per_group) {
 
 // Workspace layout of nvfp4_moe_grouped.
 struct MoeLayout {
-  size_t offsets, glist, gcount, perm, inv, rowshift, hmax, h, hq, hq_sf, slot, total;
+  size_t offsets, glist, gcount, perm, inv, rowshift, x16, hmax, hshift, h, h16, hq, hq_sf, slot, total;
 };
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared, int h_fp4) {
@@ -39,17 +39,20 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, i
   auto take = [&](size_t bytes) { const size_t o = off; off = round_up(off + bytes, 256); return o; };
   L.offsets = take(sizeof(int32_t) * (E + 2));
   L.glist = take(sizeof(int32_t) * (E + 1));
-  L.gcount = take(sizeof(int32_t));
+  L.gcount = take(sizeof(int32_t) * 2);
   L.perm = take(sizeof(int32_t) * Pt);
   L.inv = take(sizeof(int32_t) * Pt);
   L.rowshift = take(sizeof(int32_t) * T);
+  L.x16 = take(sizeof(uint16_t) * (size_t)T * H);
   L.hmax = take(sizeof(uint32_t) * Pt);
   if (h_fp4) {
-    L.h = 0;
+    L.h = L.h16 = L.hshift = 0;
     L.hq = take((size_t)Pt * (I / 2));
     L.hq_sf = take((size_t)Pt * (I / 16));
   } else {
+    L.hshift = take(sizeof(int32_t) * Pt);
     L.h = take(sizeof(float) * (size_t)Pt * I);
+    L.h16 = take(sizeof(uint16_t) * (size_t)Pt * I);
     L.hq = L.hq_sf = 0;
   }
   L.slot = take(sizeof(float) * (size_t)Pt * H);
@@ -91,8 +94,8 @@ int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int 
 
 size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   (void)N;
-  (void)K;
-  return M > 0 ? round_up(sizeof(int32_t) * (size_t)M, 256) : 0;
+  if (M <= 0 || K <= 0) return 0;
+  return round_up(sizeof(int32_t) * (size_t)M, 256) + round_up(sizeof(uint16_t) * (size_t)M * K, 256);
 }
 
 int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
@@ -100,6 +103,8 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
                  void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return NVFP4_ERR_SHAPE;
   if (K % 256 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
+  // every tensor a kernel reads through a buffer resource must span < 4 GiB
+  if (N * (K / 2) >= kMaxBuffer || M * K * 2 >= kMaxBuffer) return NVFP4_ERR_SHAPE;
   if (M == 0) return NVFP4_OK;
   const bool fp4 = x_fp4 != nullptr;
   if (fp4 && (x_bf16 || !x_sf || !gsa)) return x_bf16 ? NVFP4_ERR_ARG : NVFP4_ERR_NULL;
@@ -116,8 +121,9 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* rowshift = static_cast<int*>(workspace);
+  f16* x16 = reinterpret_cast<f16*>(static_cast<uint8_t*>(workspace) + round_up(sizeof(int32_t) * (size_t)M, 256));
   if (!fp4) {
-    hipError_t e = launch_rowshift_bf16(static_cast<const uint16_t*>(x_bf16), (int)M, (int)K, rowshift, s);
+    hipError_t e = launch_rows_to_f16(static_cast<const uint16_t*>(x_bf16), (int)M, (int)K, rowshift, x16, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
   GemmArgs g{};
@@ -128,13 +134,16 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
   g.N = (int)N;
   g.K = (int)K;
   g.M = (int)M;
-  g.a = fp4 ? static_cast<const void*>(x_fp4) : x_bf16;
+  g.list_part = 2;
+  g.a = fp4 ? static_cast<const void*>(x_fp4) : static_cast<const void*>(x16);
+  g.a_rows = (int)M;
   g.a_sf = x_sf;
-  g.rowshift = rowshift;
+  g.rowshift = fp4 ? nullptr : rowshift;
   g.gsa = fp4 ? gsa : nullptr;
   g.y = static_cast<uint16_t*>(y_bf16);
-  const int amode = fp4 ? A_FP4 : A_BF16;
-  GemmShape sh{pick_maxc((double)M), 2};
+  const int amode = fp4 ? A_FP4 : A_F16;
+  const int maxc = M <= kBigGroupRows ? 1 : pick_maxc((double)M);
+  GemmShape sh{maxc, 2};
   const int rows = gemm_rows_per_block(EPI_Y_BF16, sh);
   g.nb = (int)((N + rows - 1) / rows);
   return launch_status(launch_gemm(g, amode, EPI_Y_BF16, sh, 1, s));
@@ -152,6 +161,9 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return NVFP4_ERR_SHAPE;
   if (H % 256 != 0 || I % 256 != 0 || E > kMaxExperts || k > E) return NVFP4_ERR_SHAPE;
   if (T >= kMaxDim || H >= kMaxDim || I >= kMaxDim || T * k + T >= kMaxDim) return NVFP4_ERR_SHAPE;
+  // every tensor a kernel reads through a buffer resource must span < 4 GiB
+  if (2 * I * (H / 2) >= kMaxBuffer || T * H * 2 >= kMaxBuffer || (T * k + T) * I * 2 >= kMaxBuffer)
+    return NVFP4_ERR_SHAPE;
   if (T == 0) return NVFP4_OK;
   const bool fp4 = a->x_fp4 != nullptr;
   const bool has_shared = a->s1 != nullptr;
@@ -185,6 +197,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   int* perm = reinterpret_cast<int*>(ws + L.perm);
   int* inv = reinterpret_cast<int*>(ws + L.inv);
   int* rowshift = reinterpret_cast<int*>(ws + L.rowshift);
+  f16* x16 = reinterpret_cast<f16*>(ws + L.x16);
   unsigned* hmax = reinterpret_cast<unsigned*>(ws + L.hmax);
   float* slot = reinterpret_cast<float*>(ws + L.slot);
   const int S = has_shared ? 1 : 0;
@@ -194,8 +207,25 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   auto ev = [&](int i) {
     if (a->stage_events) (void)hipEventRecord(static_cast<hipEvent_t>(a->stage_events[i]), s);
   };
+  // Groups with more than kBigGroupRows rows run on the LDS-staged kernel; at
+  // most Pt / (kBigGroupRows + 1) groups can be that big.
+  const int n_big_max = std::min(G, Pt / (kBigGroupRows + 1));
+  const double rows_per_group = (double)Pt / (double)G;
+  const int maxc_big = rows_per_group > kBigGroupRows ? 8 : 4;
+  auto two_launches = [&](GemmArgs g, int amode, int epi, int r) -> bool {
+    // the 8-chunk LDS kernel reuses each staged B fragment across 4 fragments
+    GemmShape big{maxc_big, maxc_big >= 8 ? 4 : r}, small{1, r};
+    g.list_part = 0;
+    g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, big) - 1) /
+                 gemm_rows_per_block(epi, big));
+    if (launch_gemm(g, amode, epi, big, n_big_max, s) != hipSuccess) return false;
+    g.list_part = 1;
+    g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, small) - 1) /
+                 gemm_rows_per_block(epi, small));
+    return launch_gemm(g, amode, epi, small, G, s) == hipSuccess;
+  };
 
-  // 1. permutation, group order, bf16 row shifts, clearing of the h row maxima
+  // 1. permutation, group order, fp16 copy of x with row shifts, clearing of the h row maxima
   ev(0);
   PermuteArgs pa{};
   pa.ids = a->topk_ids;
@@ -213,12 +243,10 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   pa.x = fp4 ? nullptr : static_cast<const uint16_t*>(a->x);
   pa.H = (int)H;
   pa.rowshift = rowshift;
+  pa.x16 = x16;
   pa.zero_buf = h_fp4 ? nullptr : hmax;
   pa.n_zero = Pt;
   if (launch_permute(pa, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
-
-  const double rows_per_group = (double)Pt / (double)G;
-  const int maxc = pick_maxc(rows_per_group);
 
   // 2. gate/up GEMM with fused SwiGLU
   ev(1);
@@ -238,28 +266,33 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g1.offsets = offsets;
   g1.glist = glist;
   g1.gcount = gcount;
-  g1.a = fp4 ? static_cast<const void*>(a->x_fp4) : a->x;
+  g1.a = fp4 ? static_cast<const void*>(a->x_fp4) : static_cast<const void*>(x16);
+  g1.a_rows = (int)T;
   g1.a_sf = a->x_sf;
   g1.a_by_token = 1;
   g1.perm = perm;
   g1.topk = (int)k;
   g1.P = P;
-  g1.rowshift = rowshift;
+  g1.rowshift = fp4 ? nullptr : rowshift;
   g1.gsa = fp4 ? a->a1_gs : nullptr;
   g1.h = h_fp4 ? nullptr : reinterpret_cast<float*>(ws + L.h);
   g1.hmax = hmax;
   g1.hq = h_fp4 ? ws + L.hq : nullptr;
   g1.hq_sf = h_fp4 ? ws + L.hq_sf : nullptr;
   g1.h_gs = a->a2_gs;
-  GemmShape sh1{maxc, maxc >= 4 ? 4 : 2};
   const int epi1 = h_fp4 ? EPI_SWIGLU_FP4 : EPI_SWIGLU_F32;
-  g1.nb = (int)((I + gemm_rows_per_block(epi1, sh1) - 1) / gemm_rows_per_block(epi1, sh1));
-  if (launch_gemm(g1, fp4 ? A_FP4 : A_BF16, epi1, sh1, G, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  if (!two_launches(g1, fp4 ? A_FP4 : A_F16, epi1, 2)) return NVFP4_ERR_LAUNCH;
   if (!h_fp4 && a->a2_gs_out)
     if (launch_amax_to_gs(hmax, Pt, a->a2_gs_out, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
 
-  // 3. down GEMM, scattering each pair's row (scaled by its weight_scale_2)
+  // 3. fp16 copy of h (unless it is NVFP4), down GEMM scattering each pair's row
   ev(2);
+  int* hshift = h_fp4 ? nullptr : reinterpret_cast<int*>(ws + L.hshift);
+  f16* h16 = h_fp4 ? nullptr : reinterpret_cast<f16*>(ws + L.h16);
+  if (!h_fp4)
+    if (launch_h_to_f16(reinterpret_cast<const float*>(ws + L.h), hmax, offsets, (int)E + 1, Pt, (int)I, h16, hshift,
+                        s) != hipSuccess)
+      return NVFP4_ERR_LAUNCH;
   GemmArgs g2{};
   g2.w = a->w2;
   g2.w_sf = a->w2_sf;
@@ -275,18 +308,17 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g2.offsets = offsets;
   g2.glist = glist;
   g2.gcount = gcount;
-  g2.a = h_fp4 ? static_cast<const void*>(ws + L.hq) : static_cast<const void*>(ws + L.h);
+  g2.a = h_fp4 ? static_cast<const void*>(ws + L.hq) : static_cast<const void*>(h16);
+  g2.a_rows = Pt;
   g2.a_sf = h_fp4 ? ws + L.hq_sf : nullptr;
   g2.a_by_token = 0;
   g2.perm = perm;
   g2.topk = (int)k;
   g2.P = P;
-  g2.rowmax = hmax;
+  g2.rowshift = hshift;
   g2.gsa = h_fp4 ? a->a2_gs : nullptr;
   g2.slot = slot;
-  GemmShape sh2{maxc, 4};
-  g2.nb = (int)((H + gemm_rows_per_block(EPI_SLOT, sh2) - 1) / gemm_rows_per_block(EPI_SLOT, sh2));
-  if (launch_gemm(g2, h_fp4 ? A_FP4 : A_F32, EPI_SLOT, sh2, G, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  if (!two_launches(g2, h_fp4 ? A_FP4 : A_F16, EPI_SLOT, 2)) return NVFP4_ERR_LAUNCH;
 
   // 4. weighted combine
   ev(3);

@@ -6,6 +6,20 @@
 
 namespace nvfp4 {
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9-family descriptor:
+// stride 0, 32-bit data format word).  Loads beyond `bytes` return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // 8 E2M1 codes (element e in nibble e of `w`) times one E4M3 block scale,
 // as 8 fp16.  Exact: |E2M1 * E4M3| lies in {0} U [2^-10, 2688] and needs at
 // most 5 significant bits, which fp16 holds.  The hardware converter applies
@@ -71,6 +85,15 @@ __device__ __forceinline__ int shift_from_maxbits(uint32_t mbits) {
   if (mbits == 0u || e == 0xFFu) return 0;
   if (e == 0u) return 140;
   return 141 - (int)e;
+}
+
+// fp16 activation copies are stored step-major inside every 256-element K
+// chunk: element k = 64*g + 8*q + e of a chunk (g = MFMA lane group, q = MFMA
+// step) sits at position (4*q + g)*8 + e, so at each MFMA step the four lane
+// groups of a row read 64 contiguous bytes.  `c` is a multiple of 8.
+__device__ __forceinline__ int step_major_pos(int c) {
+  const int kk = c & 255;
+  return (c & ~255) + (((kk & 63) >> 3) * 4 + (kk >> 6)) * 8;
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }

@@ -1,34 +1,44 @@
 // Grouped NVFP4 GEMM for gfx950: weight-stationary streaming of packed E2M1
-// weights + E4M3 block scales, exact decode to fp16, fp16 MFMA, fused
-// epilogues (dense bf16 output, SwiGLU with fp32 or NVFP4 hidden output,
-// scatter of per-pair output rows).
+// weights + E4M3 block scales, exact decode to fp16, fp16 MFMA with fp32
+// accumulation, fused epilogues (dense bf16 output, SwiGLU with fp32 or NVFP4
+// hidden output, scatter of per-pair output rows).
 //
-// Computes, per group g and weight row n, acc[row, n] = sum_k A[row, k] * E2M1(W[n,k]) * E4M3(S[n,k/16])
-// and applies the product of the two global scales (weight_scale_2 of the
-// group and the activation global scale) once, in the epilogue: the block-
-// scaled GEMM y = (x*scale_a*gsa) @ (w*scale_b*gsb)^T of page
-// "nvfp4-megamoe-kernel, commit 1121cd7 - single_shot_inference.py" (note on
-// the weight-dequant global scale).
+// Per group g and weight row n: acc[row, n] = sum_k A[row, k] * E2M1(W[n,k]) * E4M3(S[n,k/16]);
+// the product of the two global scales (weight_scale_2 of the group and the
+// activation global scale) is applied once, in the epilogue: the block-scaled
+// GEMM y = (x*scale_a*gsa) @ (w*scale_b*gsb)^T of page "nvfp4-megamoe-kernel,
+// commit 1121cd7 - single_shot_inference.py" (note on the weight-dequant
+// global scale).
 //
-// Mapping (one workgroup = NW waves):
-//  * a work item is (group, block of weight rows); groups come in the order of
-//    a device-side list (largest first), so no host synchronisation is needed;
+// Common mapping:
+//  * a work item is (group, block of weight rows); groups come from a
+//    device-side list sorted by size, so no host synchronisation is needed.
+//    Groups with more than 16 rows go to the LDS kernel, the others to the
+//    direct kernel (two launches over the two parts of the list);
 //  * every wave owns R fragments of 16 weight rows and streams them over the
-//    whole K range once per pass of up to 16*MAXC activation rows: weights are
-//    read from HBM once per pass (once in total unless a group has more rows);
+//    whole K range once per pass of activation rows;
 //  * K is walked in chunks of 256.  Lane (r, g) of a fragment (r = lane%16,
 //    g = lane/16) loads bytes [32g, 32g+32) of the chunk of row r (64 codes)
-//    and the 4 scale bytes of those 4 blocks, with two 16-byte loads and one
-//    4-byte load.  MFMA step q (0..7) of the chunk then covers K positions
-//    {64g' + 8q + e}: the MFMA's K index is a permutation of the real K, the
-//    same for both operands, so the sum is unchanged;
-//  * the workgroup stages the activation chunk [16*MAXC rows, 256] into LDS as
-//    fp16 (double buffered), converted exactly: NVFP4 rows decode exactly;
-//    bf16 / fp32 rows are scaled by a per-row power of two into [2^14, 2^15)
-//    so fp16 holds them (the shift is undone in the epilogue);
+//    with two 16-byte loads, and the 4 scale bytes of those 4 blocks.  MFMA
+//    step q (0..7) covers K positions {64g' + 8q + e}: the MFMA's K index is a
+//    permutation of the real K, the same for both operands, so the sum is
+//    unchanged.  (Measured on MI355X: this pattern streams at ~6 TB/s; wider
+//    per-lane spans coalesce worse.)
 //  * weights are the MFMA A operand (16 weight rows), activations the B
-//    operand (16 tokens): D[weight row][token], so decode-sized groups waste
-//    MFMA lanes but never HBM bandwidth.
+//    operand (16 rows of tokens): D[weight row][token row];
+//  * activations arrive as fp16 rows (bf16 / fp32 values scaled by a per-row
+//    power of two into [2^14, 2^15), undone in the epilogue: exact) or as
+//    NVFP4 rows (decoded exactly; global scale in the epilogue).
+//
+// Direct kernel (groups of <= 16 rows, the decode case): no LDS and no
+// barriers.  Each lane also loads its own B fragment (the token row it holds
+// in the MFMA layout) from global memory, two chunks ahead like the weights,
+// so every wave streams independently.
+//
+// LDS kernel (bigger groups): the workgroup stages the activation chunk
+// [16*MAXC rows, 256] into LDS (double buffered) and every wave reads its B
+// fragments from there, so the activation rows are fetched once per
+// workgroup instead of once per wave.
 #include "device_util.h"
 
 namespace nvfp4 {
@@ -42,6 +52,19 @@ struct WBuf {
   uint32_t s[R];
 };
 
+// B fragment of one lane for one chunk: 8 x 8 fp16 (A_F16) or 64 codes + 4 scales (A_FP4)
+template <int AM>
+struct BBuf;
+template <>
+struct BBuf<A_F16> {
+  u32x4 v[8];
+};
+template <>
+struct BBuf<A_FP4> {
+  u32x4 c0, c1;
+  uint32_t s;
+};
+
 __device__ __forceinline__ uint32_t word_of(const u32x4& a, const u32x4& b, int q) {
   return q < 4 ? a[q & 3] : b[q & 3];
 }
@@ -49,134 +72,523 @@ __device__ __forceinline__ uint32_t word_of(const u32x4& a, const u32x4& b, int 
 template <int EP>
 constexpr bool is_swiglu() { return EP == EPI_SWIGLU_F32 || EP == EPI_SWIGLU_FP4; }
 
-// Rows (output columns) covered by one workgroup.
 template <int R, int NW, int EP>
 constexpr int block_rows() { return is_swiglu<EP>() ? NW * (R / 2) * 16 : NW * R * 16; }
 
+constexpr int kNW = 4;  // waves per workgroup
+
+// Resolved work item.
+struct Item {
+  int g, row0, m;
+  const uint8_t* W;
+  const uint8_t* WS;
+  float alpha;
+};
+
+__device__ __forceinline__ bool resolve_item(const GemmArgs& a, int gi, Item& it) {
+  if (a.offsets) {
+    const int lo = a.list_part == 1 ? a.gcount[1] : 0;
+    const int hi = a.list_part == 0 ? a.gcount[1] : a.gcount[0];
+    gi += lo;
+    if (gi >= hi) return false;
+    it.g = a.glist[gi];
+    it.row0 = a.offsets[it.g];
+    it.m = a.offsets[it.g + 1] - it.row0;
+  } else {
+    if (gi > 0) return false;
+    it.g = 0;
+    it.row0 = 0;
+    it.m = a.M;
+  }
+  if (it.m <= 0) return false;
+  const bool shared = it.g >= a.n_routed;
+  it.W = shared ? a.sw : a.w + (int64_t)it.g * a.w_gstride;
+  it.WS = shared ? a.sw_sf : a.w_sf + (int64_t)it.g * a.sf_gstride;
+  it.alpha = shared ? a.sw_ws2[0] : a.w_ws2[it.g];
+  if (a.gsa) it.alpha *= a.gsa[0];
+  return true;
+}
+
+// Activation row (in the A tensor) of sorted row r.
+__device__ __forceinline__ int a_row_of(const GemmArgs& a, int r) {
+  if (!a.a_by_token || !a.offsets) return r;
+  const int pid = a.perm[r];
+  return pid < a.P ? pid / a.topk : pid - a.P;
+}
+
+__device__ __forceinline__ int shift_of(const GemmArgs& a, int arow) {
+  return a.rowshift ? a.rowshift[arow] : 0;
+}
+
+// Weight fragments of this wave, read with buffer loads: one resource per
+// group (codes and scales), one 32-bit lane offset shared by all fragments,
+// and wave-uniform fragment offsets (scalar registers).
+template <int R, int EP>
+struct Frags {
+  int fbase[R];
+  bool fvalid[R];
+  rsrc_t rw, rs;       // codes [N, K/2], scales [N, K/16] of the group
+  uint32_t vw, vs;     // lane offsets: row lr, byte 32*lg (codes) / 4*lg (scales)
+  uint32_t sw[R], ss[R];  // fragment offsets (first row of the fragment)
+  uint32_t KB, KS;
+
+  __device__ __forceinline__ void init(const GemmArgs& a, const Item& it, int nbk, int wave, int lr, int lg) {
+    KB = a.K / 2;
+    KS = a.K / 16;
+    rw = make_rsrc(it.W, (uint32_t)a.N * KB);
+    rs = make_rsrc(it.WS, (uint32_t)a.N * KS);
+    vw = lr * KB + lg * 32;
+    vs = lr * KS + lg * 4;
+#pragma unroll
+    for (int f = 0; f < R; ++f) {
+      int row0;
+      if constexpr (is_swiglu<EP>()) {
+        const int gate = nbk * block_rows<R, kNW, EP>() + (wave * (R / 2) + (f >> 1)) * 16;
+        fbase[f] = gate;
+        fvalid[f] = gate < a.I;
+        row0 = (f & 1 ? a.I : 0) + gate;
+      } else {
+        const int base = nbk * block_rows<R, kNW, EP>() + (wave * R + f) * 16;
+        fbase[f] = base;
+        fvalid[f] = base < a.N;
+        row0 = base;
+      }
+      if (!fvalid[f]) row0 = 0;  // stay inside the group; results are discarded
+      sw[f] = (uint32_t)row0 * KB;
+      ss[f] = (uint32_t)row0 * KS;
+    }
+  }
+
+  // Codes only (scales come from load_scales4).
+  __device__ __forceinline__ void load_codes(u32x4 (&c0)[R], u32x4 (&c1)[R], int kc) const {
+#pragma unroll
+    for (int f = 0; f < R; ++f) {
+      c0[f] = buf_load16(rw, vw, sw[f] + kc * 128);
+      c1[f] = buf_load16(rw, vw + 16, sw[f] + kc * 128);
+    }
+  }
+
+  // Scale words of 4 consecutive chunks [4*sc, 4*sc+4) with one 16-byte load
+  // per lane: lane group G loads the 16 scale bytes of chunk 4*sc+G of its row
+  // (chunk index clamped to the last chunk); transpose4 then hands every lane
+  // its own 4-byte word of each of the 4 chunks.
+  __device__ __forceinline__ void load_scales4(u32x4 (&raw)[R], int sc, int nkc, int lg) const {
+    const int kc = min(4 * sc + lg, nkc - 1);
+#pragma unroll
+    for (int f = 0; f < R; ++f) raw[f] = buf_load16(rs, vs - lg * 4 + kc * 16, ss[f]);
+  }
+
+  __device__ __forceinline__ void load(WBuf<R>& wb, int kc) const {
+#pragma unroll
+    for (int f = 0; f < R; ++f) {
+      wb.c0[f] = buf_load16(rw, vw, sw[f] + kc * 128);
+      wb.c1[f] = buf_load16(rw, vw + 16, sw[f] + kc * 128);
+      wb.s[f] = buf_load4(rs, vs, ss[f] + kc * 16);
+    }
+  }
+};
+
+// 4x4 transpose of dwords across the four 16-lane groups: on entry lane group
+// G holds v[j] = X[G][j]; on exit it holds v[c] = X[c][G].
+__device__ __forceinline__ void transpose4(u32x4& v) {
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v[0] = c[0];
+  v[1] = c[1];
+  v[2] = d[0];
+  v[3] = d[1];
+}
+
+// Epilogue for one pass.  acc[f][c]: fragment f, token chunk c; lane holds
+// D rows 4*lg..4*lg+3 of the fragment for token row pbase + 16c + lr.
+// Rows at or past `mlim` (end of this pass) are not written.
+template <int R, int MAXC, int EP>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, const Frags<R, EP>& fr,
+                                         f32x4 (&acc)[R][MAXC], int nc, int pbase, int mlim, int lr, int lg) {
+  if constexpr (EP == EPI_Y_BF16 || EP == EPI_SLOT) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int tr = pbase + 16 * c + lr;
+      if (c >= nc || tr >= mlim) continue;
+      const int r = it.row0 + tr;
+      const int sh = shift_of(a, a_row_of(a, r));
+#pragma unroll
+      for (int f = 0; f < R; ++f) {
+        if (!fr.fvalid[f]) continue;
+        const int n0 = fr.fbase[f] + 4 * lg;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh) * it.alpha;
+        if constexpr (EP == EPI_Y_BF16) {
+          uint2 o;
+          o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+          o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<uint2*>(a.y + (int64_t)r * a.N + n0) = o;
+        } else {
+          const int pid = a.perm[r];
+          *reinterpret_cast<float4*>(a.slot + (int64_t)pid * a.N + n0) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+  } else {
+    // SwiGLU: fragments 2p (gate rows) and 2p+1 (up rows) share the layout
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      if (c >= nc) continue;  // uniform across the workgroup
+      const int tr = pbase + 16 * c + lr;
+      const bool tv = tr < mlim;
+      const int r = it.row0 + (tv ? tr : 0);
+      const int sh = tv ? shift_of(a, a_row_of(a, r)) : 0;
+      float hmx = 0.f;
+#pragma unroll
+      for (int p = 0; p < R / 2; ++p) {
+        if (!fr.fvalid[2 * p]) continue;  // uniform across the wave
+        const int n0 = fr.fbase[2 * p] + 4 * lg;
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gv = __builtin_ldexpf(acc[2 * p][c][i], -sh) * it.alpha;
+          const float uv = __builtin_ldexpf(acc[2 * p + 1][c][i], -sh) * it.alpha;
+          hv[i] = gv / (1.0f + __expf(-gv)) * uv;
+        }
+        if constexpr (EP == EPI_SWIGLU_F32) {
+          if (tv) *reinterpret_cast<float4*>(a.h + (int64_t)r * a.I + n0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hmx = fmaxf(hmx, __builtin_fabsf(hv[i]));
+        } else {
+          // NVFP4 quantization of h: the fragment's 16 gate rows are one
+          // 16-element block of row r; its 4 lanes hold 4 values each.
+          float ab = fmaxf(fmaxf(__builtin_fabsf(hv[0]), __builtin_fabsf(hv[1])),
+                           fmaxf(__builtin_fabsf(hv[2]), __builtin_fabsf(hv[3])));
+          ab = fmaxf(ab, __shfl_xor(ab, 16));
+          ab = fmaxf(ab, __shfl_xor(ab, 32));
+          const float gs = a.h_gs[0];
+          uint32_t sbyte = 0, packed = 0;
+          if (gs != 0.0f) {
+            sbyte = e4m3_encode_nonneg(ab / (6.0f * gs));
+            const float scale = e4m3_to_float(sbyte) * gs;
+            if (scale != 0.0f) {
+              const float rcp = 1.0f / scale;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) packed |= e2m1_encode(hv[i] * rcp) << (4 * i);
+            }
+          }
+          if (tv) {
+            *reinterpret_cast<uint16_t*>(a.hq + (int64_t)r * (a.I / 2) + n0 / 2) = (uint16_t)packed;
+            if (lg == 0) a.hq_sf[(int64_t)r * (a.I / 16) + fr.fbase[2 * p] / 16] = (uint8_t)sbyte;
+          }
+        }
+      }
+      if constexpr (EP == EPI_SWIGLU_F32) {
+        hmx = fmaxf(hmx, __shfl_xor(hmx, 16));
+        hmx = fmaxf(hmx, __shfl_xor(hmx, 32));
+        if (tv && lg == 0) atomicMax(a.hmax + r, __float_as_uint(hmx));
+      }
+    }
+  }
+}
+
 }  // namespace
 
-template <int MAXC, int R, int NW, int AM, int EP>
-__global__ __launch_bounds__(NW * 64) void nvfp4_grouped_gemm(const GemmArgs a) {
+// ---------------------------------------------------------------------------
+// compact kernel: fp16 activations, at most kSmallRows rows per pass
+// ---------------------------------------------------------------------------
+//
+// Per 256-K chunk a wave issues 2 code loads per fragment, 1/4 scale load per
+// fragment (4 chunks of scales per load, transposed across lane groups) and
+// ceil(rows/2) activation loads: lanes 0-31 load 512 bytes of one row, lanes
+// 32-63 of the next.  The activation rows go through a wave-private LDS slot
+// (LDS operations of one wave complete in order, so no barrier is needed) and
+// are read back in the MFMA layout; lanes of absent rows read row 0 (their
+// columns are discarded).  Activations are loaded two chunks ahead, weights
+// two chunks ahead, scales one 4-chunk group ahead.
+
+constexpr int kSmallRows = 4;
+constexpr int kSlotPitch = kChunk * 2 + 64;           // bytes per staged row (bank-shifted)
+constexpr int kSlotBytes = kSmallRows * kSlotPitch;   // one chunk of up to 4 rows
+
+template <int R, int EP>
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void nvfp4_gemm_compact(const GemmArgs a) {
   static_assert(!is_swiglu<EP>() || (R % 2 == 0), "SwiGLU needs gate/up fragment pairs");
-  constexpr int PR = 16 * MAXC;          // activation rows per pass
-  constexpr int TPR = 32;                // threads per staged row (8 elements each)
-  constexpr int RSTEP = NW * 64 / TPR;   // rows staged per thread sweep
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kNW][2][kSlotBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  Item it;
+  if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
+  const int nbk = blockIdx.x % a.nb;
+  Frags<R, EP> fr;
+  fr.init(a, it, nbk, wave, lr, lg);
+  const int K = a.K;
+  const int nkc = K / kChunk;
+  const int last = nkc - 1;
+  const rsrc_t rb = make_rsrc(a.a, (uint32_t)a.a_rows * K * 2);
+  uint8_t* slot0 = &lds[wave][0][0];
+  uint8_t* slot1 = &lds[wave][1][0];
+
+  const int npass = (it.m + kSmallRows - 1) / kSmallRows;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int pbase = pass * kSmallRows;
+    const int prow = min(kSmallRows, it.m - pbase);
+    const bool two = prow > 2;                     // second compact load needed
+    // compact load lanes: row (lane/32) and (lane/32)+2 of this pass, 16 bytes at (lane%32)*16
+    const int cr0 = lane >> 5, cr1 = cr0 + 2;
+    const uint32_t vb0 = cr0 < prow ? (uint32_t)a_row_of(a, it.row0 + pbase + cr0) * K * 2 + (lane & 31) * 16
+                                    : 0x80000000u;
+    const uint32_t vb1 = cr1 < prow ? (uint32_t)a_row_of(a, it.row0 + pbase + cr1) * K * 2 + (lane & 31) * 16
+                                    : 0x80000000u;
+    const int wr0 = cr0 * kSlotPitch + (lane & 31) * 16;
+    const int wr1 = cr1 * kSlotPitch + (lane & 31) * 16;
+    // MFMA-layout read: row lr of the pass (row 0 for absent rows), step-major column
+    const int rd = (lr < prow ? lr : 0) * kSlotPitch + lg * 16;
+
+    f32x4 acc[R][1];
+#pragma unroll
+    for (int f = 0; f < R; ++f) acc[f][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    u32x4 bq0a, bq0b, bq1a, bq1b;   // compact activation loads, two chunks in flight
+    auto bload = [&](u32x4& x, u32x4& y, int kc) {
+      x = buf_load16(rb, vb0, kc * kChunk * 2);
+      if (two) y = buf_load16(rb, vb1, kc * kChunk * 2);
+    };
+    auto bstore = [&](uint8_t* slot, const u32x4& x, const u32x4& y) {
+      *reinterpret_cast<u32x4*>(slot + wr0) = x;
+      if (two) *reinterpret_cast<u32x4*>(slot + wr1) = y;
+    };
+
+    u32x4 wc0a[R], wc1a[R], wc0b[R], wc1b[R];   // codes of two chunks in flight
+    u32x4 sraw[R];                              // scales of the next 4-chunk group
+    u32x4 scur[R];                              // this lane's scale word of each chunk of the group
+
+    auto compute = [&](const u32x4 (&c0)[R], const u32x4 (&c1)[R], const uint8_t* slot, int c4) {
+      f16 sc[R][4];
+#pragma unroll
+      for (int f = 0; f < R; ++f) scales4(scur[f][c4], sc[f]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f16x8 bf = *reinterpret_cast<const f16x8*>(slot + rd + q * 64);
+#pragma unroll
+        for (int f = 0; f < R; ++f) {
+          const f16x8 af = decode8(word_of(c0[f], c1[f], q), sc[f][q >> 1]);
+          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[f][0], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // prologue
+    fr.load_scales4(sraw, 0, nkc, lg);
+    bload(bq0a, bq0b, 0);
+    bload(bq1a, bq1b, min(1, last));
+    fr.load_codes(wc0a, wc1a, 0);
+    fr.load_codes(wc0b, wc1b, min(1, last));
+    bstore(slot0, bq0a, bq0b);
+    bload(bq0a, bq0b, min(2, last));
+
+    // one iteration = one group of 4 chunks; chunk kc uses codes set (kc%2),
+    // activation slot (kc%2); at its end the activations of chunk kc+1 are
+    // stored to slot ((kc+1)%2) and chunk kc+3 is requested
+    for (int kc = 0; kc < nkc; kc += 4) {
+#pragma unroll
+      for (int f = 0; f < R; ++f) {
+        scur[f] = sraw[f];
+        transpose4(scur[f]);
+      }
+      fr.load_scales4(sraw, kc / 4 + 1, nkc, lg);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int k = kc + c4;
+        if (k >= nkc) break;
+        if ((c4 & 1) == 0) {
+          compute(wc0a, wc1a, slot0, c4);
+          fr.load_codes(wc0a, wc1a, min(k + 2, last));
+          bstore(slot1, bq1a, bq1b);
+          bload(bq1a, bq1b, min(k + 3, last));
+        } else {
+          compute(wc0b, wc1b, slot1, c4);
+          fr.load_codes(wc0b, wc1b, min(k + 2, last));
+          bstore(slot0, bq0a, bq0b);
+          bload(bq0a, bq0b, min(k + 3, last));
+        }
+      }
+    }
+    epilogue<R, 1, EP>(a, it, fr, acc, 1, pbase, pbase + prow, lr, lg);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// direct kernel: one 16-row activation chunk per pass, no LDS, no barriers
+// ---------------------------------------------------------------------------
+
+template <int R, int AM, int EP>
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void nvfp4_gemm_direct(const GemmArgs a) {
+  static_assert(!is_swiglu<EP>() || (R % 2 == 0), "SwiGLU needs gate/up fragment pairs");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  Item it;
+  if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
+  const int nbk = blockIdx.x % a.nb;
+  Frags<R, EP> fr;
+  fr.init(a, it, nbk, wave, lr, lg);
+  const int K = a.K;
+  const int nkc = K / kChunk;
+
+  const int npass = (it.m + 15) >> 4;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int pbase = pass * 16;
+    const int tr = pbase + lr;
+    const bool bv = tr < it.m;
+    const int arow = bv ? a_row_of(a, it.row0 + tr) : 0;
+    // this lane's B fragment source.  Lanes past the group's rows get an
+    // offset beyond the buffer: their loads return zeros without touching
+    // memory (their MFMA columns are discarded anyway).
+    constexpr uint32_t kOut = 0x80000000u;
+    rsrc_t rb, rbs;
+    uint32_t vb, vbs = 0;
+    if constexpr (AM == A_F16) {
+      rb = make_rsrc(a.a, (uint32_t)a.a_rows * K * 2);
+      vb = bv ? (uint32_t)arow * K * 2 + lg * 16 : kOut;   // step-major rows
+    } else {
+      rb = make_rsrc(a.a, (uint32_t)a.a_rows * (K / 2));
+      rbs = make_rsrc(a.a_sf, (uint32_t)a.a_rows * (K / 16));
+      vb = bv ? (uint32_t)arow * (K / 2) + lg * 32 : kOut;
+      vbs = bv ? (uint32_t)arow * (K / 16) + lg * 4 : kOut;
+    }
+
+    f32x4 acc[R][1];
+#pragma unroll
+    for (int f = 0; f < R; ++f) acc[f][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // B fragments: fp16 rows use a rolling prefetch (the register of step q
+    // is refilled with the next chunk's step q right after use); NVFP4 rows
+    // are double buffered like the weights.
+    BBuf<AM> bb0, bb1;
+    auto bload = [&](BBuf<AM>& b, int kc) {
+      if constexpr (AM == A_F16) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) b.v[q] = buf_load16(rb, vb, kc * kChunk * 2 + q * 64);
+      } else {
+        b.c0 = buf_load16(rb, vb, kc * 128);
+        b.c1 = buf_load16(rb, vb + 16, kc * 128);
+        b.s = buf_load4(rbs, vbs, kc * 16);
+      }
+    };
+
+    // next_kc: chunk whose B fragments refill the registers (rolling prefetch
+    // for fp16 rows); always a valid chunk, so every load is unconditional
+    auto compute = [&](const WBuf<R>& wb, BBuf<AM>& b, int next_kc) {
+      f16 sc[R][4];
+#pragma unroll
+      for (int f = 0; f < R; ++f) scales4(wb.s[f], sc[f]);
+      f16 bsc[4];
+      if constexpr (AM == A_FP4) scales4(b.s, bsc);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        f16x8 bf;
+        if constexpr (AM == A_F16) {
+          bf = __builtin_bit_cast(f16x8, b.v[q]);
+          b.v[q] = buf_load16(rb, vb, next_kc * kChunk * 2 + q * 64);
+        } else {
+          bf = decode8(word_of(b.c0, b.c1, q), bsc[q >> 1]);
+        }
+#pragma unroll
+        for (int f = 0; f < R; ++f) {
+          const f16x8 af = decode8(word_of(wb.c0[f], wb.c1[f], q), sc[f][q >> 1]);
+          acc[f][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[f][0], 0, 0, 0);
+        }
+        // keep each step's decode next to its MFMAs (bounds register pressure;
+        // the MFMAs still overlap the next step's VALU decode)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Prefetch: weights two chunks ahead (wb0 / wb1), B one chunk ahead.
+    // Chunk indices are clamped to the last chunk, so the loads past the end
+    // re-read it (in bounds, results unused) instead of branching.
+    const int last = nkc - 1;
+    WBuf<R> wb0, wb1;
+    fr.load(wb0, 0);
+    bload(bb0, 0);
+    fr.load(wb1, min(1, last));
+    if constexpr (AM == A_FP4) bload(bb1, min(1, last));
+    for (int kc = 0; kc < nkc; kc += 2) {
+      if constexpr (AM == A_F16) {
+        compute(wb0, bb0, min(kc + 1, last));
+      } else {
+        compute(wb0, bb0, 0);
+        bload(bb0, min(kc + 2, last));
+      }
+      fr.load(wb0, min(kc + 2, last));
+      if (kc + 1 >= nkc) break;
+      if constexpr (AM == A_F16) {
+        compute(wb1, bb0, min(kc + 2, last));
+      } else {
+        compute(wb1, bb1, 0);
+        bload(bb1, min(kc + 3, last));
+      }
+      fr.load(wb1, min(kc + 3, last));
+    }
+    epilogue<R, 1, EP>(a, it, fr, acc, 1, pbase, min(it.m, pbase + 16), lr, lg);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS kernel: activation chunks staged per workgroup
+// ---------------------------------------------------------------------------
+
+template <int MAXC, int R, int AM, int EP>
+__global__ __launch_bounds__(kNW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
+  static_assert(!is_swiglu<EP>() || (R % 2 == 0), "SwiGLU needs gate/up fragment pairs");
+  constexpr int PR = 16 * MAXC;         // activation rows per pass
+  constexpr int TPR = 32;               // threads per staged row (8 elements each)
+  constexpr int RSTEP = kNW * 64 / TPR; // rows staged per thread sweep
   constexpr int SROWS = (PR + RSTEP - 1) / RSTEP;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][PR * kLdsRow];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-
-  // ---- work item: (group, block of weight rows)
-  const int gi = blockIdx.x / a.nb;
-  const int nbk = blockIdx.x - gi * a.nb;
-  int g, row0, m;
-  if (a.offsets) {
-    if (gi >= *a.gcount) return;
-    g = a.glist[gi];
-    row0 = a.offsets[g];
-    m = a.offsets[g + 1] - row0;
-  } else {
-    g = 0;
-    row0 = 0;
-    m = a.M;
-  }
-  if (m <= 0) return;
-  const bool shared = g >= a.n_routed;
-  const uint8_t* W = shared ? a.sw : a.w + (int64_t)g * a.w_gstride;
-  const uint8_t* WS = shared ? a.sw_sf : a.w_sf + (int64_t)g * a.sf_gstride;
-  float alpha = shared ? a.sw_ws2[0] : a.w_ws2[g];
-  if (a.gsa) alpha *= a.gsa[0];
-
+  Item it;
+  if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
+  const int nbk = blockIdx.x % a.nb;
+  Frags<R, EP> fr;
+  fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
   const int64_t KB = K / 2, KS = K / 16;
   const int nkc = K / kChunk;
-
-  // ---- this wave's weight fragments
-  int fbase[R];       // first weight row of the fragment (gate row for SwiGLU pairs)
-  bool fvalid[R];
-  const uint8_t* wp[R];
-  const uint8_t* sp[R];
-#pragma unroll
-  for (int f = 0; f < R; ++f) {
-    int row;
-    if constexpr (is_swiglu<EP>()) {
-      const int gate = nbk * block_rows<R, NW, EP>() + (wave * (R / 2) + (f >> 1)) * 16;
-      fbase[f] = gate;
-      fvalid[f] = gate < a.I;
-      row = (f & 1 ? a.I : 0) + gate + lr;
-    } else {
-      const int base = nbk * block_rows<R, NW, EP>() + (wave * R + f) * 16;
-      fbase[f] = base;
-      fvalid[f] = base < a.N;
-      row = base + lr;
-    }
-    if (!fvalid[f]) row = lr;  // keep addresses inside the group; results are discarded
-    wp[f] = W + (int64_t)row * KB + lg * 32;
-    sp[f] = WS + (int64_t)row * KS + lg * 4;
-  }
-
-  auto wload = [&](WBuf<R>& wb, int kc) {
-#pragma unroll
-    for (int f = 0; f < R; ++f) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(wp[f] + (int64_t)kc * 128);
-      wb.c0[f] = __builtin_nontemporal_load(p);
-      wb.c1[f] = __builtin_nontemporal_load(p + 1);
-      wb.s[f] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp[f] + (int64_t)kc * 16));
-    }
-  };
-
-  // A row (in the activation tensor) of sorted row r, and its staging shift.
-  auto a_row_of = [&](int r) -> int {
-    if (!a.a_by_token || !a.offsets) return r;
-    const int pid = a.perm[r];
-    return pid < a.P ? pid / a.topk : pid - a.P;
-  };
-  auto shift_of = [&](int arow) -> int {
-    if constexpr (AM == A_BF16) return a.rowshift[arow];
-    else if constexpr (AM == A_F32) return shift_from_maxbits(a.rowmax[arow]);
-    else return 0;
-  };
-
-  const int seg = tid % TPR;       // 8-element segment of the 256-element chunk
+  const int seg = tid % TPR;
   const int rsub = tid / TPR;
 
-  const int npass = (m + PR - 1) / PR;
+  const int npass = (it.m + PR - 1) / PR;
   for (int pass = 0; pass < npass; ++pass) {
     const int pbase = pass * PR;
-    const int prow = min(PR, m - pbase);
+    const int prow = min(PR, it.m - pbase);
     const int nc = (prow + 15) >> 4;
 
-    // staging rows of this thread
     int srow[SROWS];
-    int sshift[SROWS];
     bool sval[SROWS];
 #pragma unroll
     for (int i = 0; i < SROWS; ++i) {
       const int rr = rsub + RSTEP * i;
       sval[i] = rr < prow;
-      const int arow = sval[i] ? a_row_of(row0 + pbase + rr) : 0;
-      srow[i] = arow;
-      sshift[i] = sval[i] ? shift_of(arow) : 0;
+      srow[i] = sval[i] ? a_row_of(a, it.row0 + pbase + rr) : 0;
     }
-
-    // staging registers
-    uint4 st0[SROWS];
-    uint4 st1[SROWS];  // A_F32 second half
+    u32x4 st0[SROWS];
     uint32_t stc[SROWS], sts[SROWS];
 
     auto stage_load = [&](int kc) {
 #pragma unroll
       for (int i = 0; i < SROWS; ++i) {
         if (!sval[i]) continue;
-        if constexpr (AM == A_BF16) {
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(a.a) + (int64_t)srow[i] * K + kc * kChunk + seg * 8;
-          st0[i] = *reinterpret_cast<const uint4*>(src);
-        } else if constexpr (AM == A_F32) {
-          const float* src = reinterpret_cast<const float*>(a.a) + (int64_t)srow[i] * K + kc * kChunk + seg * 8;
-          st0[i] = *reinterpret_cast<const uint4*>(src);
-          st1[i] = *reinterpret_cast<const uint4*>(src + 4);
+        if constexpr (AM == A_F16) {
+          st0[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.a) +
+                                                   ((int64_t)srow[i] * K + kc * kChunk + seg * 8) * 2);
         } else {
           const uint8_t* src = reinterpret_cast<const uint8_t*>(a.a) + (int64_t)srow[i] * KB + kc * 128 + seg * 4;
           stc[i] = *reinterpret_cast<const uint32_t*>(src);
@@ -190,20 +602,8 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_grouped_gemm(const GemmArgs a) 
         if (!sval[i]) continue;
         const int rr = rsub + RSTEP * i;
         f16x8 v;
-        if constexpr (AM == A_BF16) {
-          const uint32_t u[4] = {st0[i].x, st0[i].y, st0[i].z, st0[i].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] = (f16)__builtin_ldexpf(bf16_bits_to_float(u[e] & 0xFFFFu), sshift[i]);
-            v[2 * e + 1] = (f16)__builtin_ldexpf(bf16_bits_to_float(u[e] >> 16), sshift[i]);
-          }
-        } else if constexpr (AM == A_F32) {
-          const uint32_t u[8] = {st0[i].x, st0[i].y, st0[i].z, st0[i].w, st1[i].x, st1[i].y, st1[i].z, st1[i].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (f16)__builtin_ldexpf(__uint_as_float(u[e]), sshift[i]);
-        } else {
-          v = decode8(stc[i], (f16)e4m3_to_float(sts[i]));
-        }
+        if constexpr (AM == A_F16) v = __builtin_bit_cast(f16x8, st0[i]);
+        else v = decode8(stc[i], (f16)e4m3_to_float(sts[i]));
         *reinterpret_cast<f16x8*>(&lds[buf][rr * kLdsRow + seg * 16]) = v;
       }
     };
@@ -227,7 +627,10 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_grouped_gemm(const GemmArgs a) 
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
           if (c < nc) {
-            const f16x8 b = *reinterpret_cast<const f16x8*>(B + (16 * c + lr) * kLdsRow + (64 * lg + 8 * q) * 2);
+            // fp16 rows are staged in their step-major order; NVFP4 rows are
+            // decoded into natural order
+            const int col = AM == A_F16 ? (4 * q + lg) * 16 : (64 * lg + 8 * q) * 2;
+            const f16x8 b = *reinterpret_cast<const f16x8*>(B + (16 * c + lr) * kLdsRow + col);
 #pragma unroll
             for (int f = 0; f < R; ++f)
               acc[f][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], b, acc[f][c], 0, 0, 0);
@@ -237,109 +640,25 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_grouped_gemm(const GemmArgs a) 
     };
 
     WBuf<R> wb0, wb1;
-    wload(wb0, 0);
-    if (nkc > 1) wload(wb1, 1);
+    fr.load(wb0, 0);
+    if (nkc > 1) fr.load(wb1, 1);
     stage_load(0);
     stage_write(0);
     __syncthreads();
     for (int kc = 0; kc < nkc; kc += 2) {
-      // chunk kc: weights in wb0, activations in LDS buffer 0
       if (kc + 1 < nkc) stage_load(kc + 1);
       compute(wb0, 0);
-      if (kc + 2 < nkc) wload(wb0, kc + 2);
+      if (kc + 2 < nkc) fr.load(wb0, kc + 2);
       if (kc + 1 < nkc) stage_write(1);
       __syncthreads();
       if (kc + 1 >= nkc) break;
-      // chunk kc+1: weights in wb1, activations in LDS buffer 1
       if (kc + 2 < nkc) stage_load(kc + 2);
       compute(wb1, 1);
-      if (kc + 3 < nkc) wload(wb1, kc + 3);
+      if (kc + 3 < nkc) fr.load(wb1, kc + 3);
       if (kc + 2 < nkc) stage_write(0);
       __syncthreads();
     }
-
-    // ---- epilogue
-    if constexpr (EP == EPI_Y_BF16 || EP == EPI_SLOT) {
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        const int tr = pbase + 16 * c + lr;
-        if (c >= nc || tr >= m) continue;
-        const int r = row0 + tr;
-        const int sh = shift_of(a_row_of(r));
-#pragma unroll
-        for (int f = 0; f < R; ++f) {
-          if (!fvalid[f]) continue;
-          const int n0 = fbase[f] + 4 * lg;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh) * alpha;
-          if constexpr (EP == EPI_Y_BF16) {
-            uint2 o;
-            o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
-            o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(a.y + (int64_t)r * a.N + n0) = o;
-          } else {
-            const int pid = a.perm[r];
-            *reinterpret_cast<float4*>(a.slot + (int64_t)pid * a.N + n0) = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
-      }
-    } else {
-      // SwiGLU: fragments 2p (gate rows) and 2p+1 (up rows) share the layout
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        if (c >= nc) continue;   // uniform across the wave
-        const int tr = pbase + 16 * c + lr;
-        const bool tv = tr < m;
-        const int r = row0 + (tv ? tr : 0);
-        const int sh = tv ? shift_of(a_row_of(r)) : 0;
-        float hmx = 0.f;
-#pragma unroll
-        for (int p = 0; p < R / 2; ++p) {
-          if (!fvalid[2 * p]) continue;  // uniform across the wave
-          const int n0 = fbase[2 * p] + 4 * lg;
-          float hv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float gv = __builtin_ldexpf(acc[2 * p][c][i], -sh) * alpha;
-            const float uv = __builtin_ldexpf(acc[2 * p + 1][c][i], -sh) * alpha;
-            hv[i] = gv / (1.0f + __expf(-gv)) * uv;
-          }
-          if constexpr (EP == EPI_SWIGLU_F32) {
-            if (tv) *reinterpret_cast<float4*>(a.h + (int64_t)r * a.I + n0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hmx = fmaxf(hmx, __builtin_fabsf(hv[i]));
-          } else {
-            // NVFP4 quantization of h: the fragment's 16 gate rows are one
-            // 16-element block of row r; its 4 lanes hold 4 values each.
-            float ab = fmaxf(fmaxf(__builtin_fabsf(hv[0]), __builtin_fabsf(hv[1])),
-                             fmaxf(__builtin_fabsf(hv[2]), __builtin_fabsf(hv[3])));
-            ab = fmaxf(ab, __shfl_xor(ab, 16));
-            ab = fmaxf(ab, __shfl_xor(ab, 32));
-            const float gs = a.h_gs[0];
-            uint32_t sbyte = 0, packed = 0;
-            if (gs != 0.0f) {
-              sbyte = e4m3_encode_nonneg(ab / (6.0f * gs));
-              const float scale = e4m3_to_float(sbyte) * gs;
-              if (scale != 0.0f) {
-                const float rcp = 1.0f / scale;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) packed |= e2m1_encode(hv[i] * rcp) << (4 * i);
-              }
-            }
-            if (tv) {
-              *reinterpret_cast<uint16_t*>(a.hq + (int64_t)r * (a.I / 2) + n0 / 2) = (uint16_t)packed;
-              if (lg == 0) a.hq_sf[(int64_t)r * (a.I / 16) + fbase[2 * p] / 16] = (uint8_t)sbyte;
-            }
-          }
-        }
-        if constexpr (EP == EPI_SWIGLU_F32) {
-          hmx = fmaxf(hmx, __shfl_xor(hmx, 16));
-          hmx = fmaxf(hmx, __shfl_xor(hmx, 32));
-          if (tv && lg == 0) atomicMax(a.hmax + r, __float_as_uint(hmx));
-        }
-      }
-    }
+    epilogue<R, MAXC, EP>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
   }
 }
 
@@ -348,35 +667,46 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_grouped_gemm(const GemmArgs a) 
 // ---------------------------------------------------------------------------
 
 namespace {
-constexpr int kNW = 4;
 
-template <int MAXC, int R, int AM, int EP>
-hipError_t launch_one(const GemmArgs& a, int n_groups, hipStream_t s) {
-  const int grid = n_groups * a.nb;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((nvfp4_grouped_gemm<MAXC, R, kNW, AM, EP>), dim3(grid), dim3(kNW * 64), 0, s, a);
+template <int AM, int EP, int R>
+hipError_t launch_direct(const GemmArgs& a, int n_items, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  if constexpr (AM == A_F16)
+    hipLaunchKernelGGL((nvfp4_gemm_compact<R, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((nvfp4_gemm_direct<R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int AM, int EP, int R>
-hipError_t by_maxc(const GemmArgs& a, int maxc, int n_groups, hipStream_t s) {
+hipError_t launch_lds(const GemmArgs& a, int maxc, int n_items, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
   switch (maxc) {
-    case 1: return launch_one<1, R, AM, EP>(a, n_groups, s);
-    case 2: return launch_one<2, R, AM, EP>(a, n_groups, s);
-    case 4: return launch_one<4, R, AM, EP>(a, n_groups, s);
-    case 8: return launch_one<8, R, AM, EP>(a, n_groups, s);
+    case 2: hipLaunchKernelGGL((nvfp4_gemm_lds<2, R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((nvfp4_gemm_lds<4, R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((nvfp4_gemm_lds<8, R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int AM, int EP>
+hipError_t dispatch(const GemmArgs& a, GemmShape sh, int n_groups, hipStream_t s) {
+  const int n_items = n_groups * a.nb;
+  if (sh.maxc == 1) {
+    switch (sh.r) {
+      case 2: return launch_direct<AM, EP, 2>(a, n_items, s);
+      case 4: return launch_direct<AM, EP, 4>(a, n_items, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (sh.r) {
+    case 2: return launch_lds<AM, EP, 2>(a, sh.maxc, n_items, s);
+    case 4: return launch_lds<AM, EP, 4>(a, sh.maxc, n_items, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int AM, int EP>
-hipError_t by_r(const GemmArgs& a, GemmShape sh, int n_groups, hipStream_t s) {
-  switch (sh.r) {
-    case 2: return by_maxc<AM, EP, 2>(a, sh.maxc, n_groups, s);
-    case 4: return by_maxc<AM, EP, 4>(a, sh.maxc, n_groups, s);
-    default: return hipErrorInvalidValue;
-  }
-}
 }  // namespace
 
 int gemm_rows_per_block(int epi, GemmShape sh) {
@@ -385,15 +715,14 @@ int gemm_rows_per_block(int epi, GemmShape sh) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, GemmShape sh, int n_groups, hipStream_t s) {
-  // valid (activation, epilogue) pairs
-  if (amode == A_BF16 && epi == EPI_Y_BF16) return by_r<A_BF16, EPI_Y_BF16>(a, sh, n_groups, s);
-  if (amode == A_FP4 && epi == EPI_Y_BF16) return by_r<A_FP4, EPI_Y_BF16>(a, sh, n_groups, s);
-  if (amode == A_BF16 && epi == EPI_SWIGLU_F32) return by_r<A_BF16, EPI_SWIGLU_F32>(a, sh, n_groups, s);
-  if (amode == A_BF16 && epi == EPI_SWIGLU_FP4) return by_r<A_BF16, EPI_SWIGLU_FP4>(a, sh, n_groups, s);
-  if (amode == A_FP4 && epi == EPI_SWIGLU_F32) return by_r<A_FP4, EPI_SWIGLU_F32>(a, sh, n_groups, s);
-  if (amode == A_FP4 && epi == EPI_SWIGLU_FP4) return by_r<A_FP4, EPI_SWIGLU_FP4>(a, sh, n_groups, s);
-  if (amode == A_F32 && epi == EPI_SLOT) return by_r<A_F32, EPI_SLOT>(a, sh, n_groups, s);
-  if (amode == A_FP4 && epi == EPI_SLOT) return by_r<A_FP4, EPI_SLOT>(a, sh, n_groups, s);
+  if (amode == A_F16 && epi == EPI_Y_BF16) return dispatch<A_F16, EPI_Y_BF16>(a, sh, n_groups, s);
+  if (amode == A_FP4 && epi == EPI_Y_BF16) return dispatch<A_FP4, EPI_Y_BF16>(a, sh, n_groups, s);
+  if (amode == A_F16 && epi == EPI_SWIGLU_F32) return dispatch<A_F16, EPI_SWIGLU_F32>(a, sh, n_groups, s);
+  if (amode == A_F16 && epi == EPI_SWIGLU_FP4) return dispatch<A_F16, EPI_SWIGLU_FP4>(a, sh, n_groups, s);
+  if (amode == A_FP4 && epi == EPI_SWIGLU_F32) return dispatch<A_FP4, EPI_SWIGLU_F32>(a, sh, n_groups, s);
+  if (amode == A_FP4 && epi == EPI_SWIGLU_FP4) return dispatch<A_FP4, EPI_SWIGLU_FP4>(a, sh, n_groups, s);
+  if (amode == A_F16 && epi == EPI_SLOT) return dispatch<A_F16, EPI_SLOT>(a, sh, n_groups, s);
+  if (amode == A_FP4 && epi == EPI_SLOT) return dispatch<A_FP4, EPI_SLOT>(a, sh, n_groups, s);
   return hipErrorInvalidValue;
 }
 

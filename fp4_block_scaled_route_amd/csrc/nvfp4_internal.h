@@ -21,10 +21,13 @@ constexpr int kLdsRow = kChunk * 2 + 16;
 
 // Activation operand sources of the grouped GEMM.
 enum AMode {
-  A_BF16 = 0,  // bf16 rows, widened to fp16 with a per-row power-of-two shift
-  A_F32 = 1,   // fp32 rows (hidden h), same per-row shift taken from a row max
+  A_F16 = 0,   // fp16 rows holding bf16/fp32 values times 2^rowshift[row] (exact)
   A_FP4 = 2    // NVFP4 rows, decoded exactly to fp16 (global scale in the epilogue)
 };
+
+// Groups with more rows than this go to the LDS-staged GEMM kernel; smaller
+// ones to the barrier-free kernels (fp16 activations: at most 4 rows per pass).
+constexpr int kBigGroupRows = 4;
 
 // Epilogues of the grouped GEMM.
 enum EpiMode {
@@ -49,21 +52,25 @@ struct GemmArgs {
   int K;               // reduction length (multiple of 256)
   int I;               // gate/up split: gate rows [0, I), up rows [I, 2I) (SwiGLU epilogues)
   // Groups: rows of group g are [off[g], off[g+1]) of the sorted row space;
-  // glist/gcount give the processing order.  Dense: offsets == nullptr, rows [0, M).
+  // glist gives the processing order (largest first); gcount[0] = non-empty
+  // groups, gcount[1] = groups with more than kBigGroupRows rows.  list_part:
+  // 0 = the big groups, 1 = the others, 2 = all.
+  // Dense: offsets == nullptr, one group of rows [0, M).
   const int* offsets;
   const int* glist;
   const int* gcount;
+  int list_part;
   int M;               // dense row count
   int nb;              // weight-row blocks per group (grid = groups * nb)
   // Activation operand.
   const void* a;       // see AMode; row pitch in elements = K
+  int a_rows;          // rows of the activation tensor (bounds of its buffer resource)
   const uint8_t* a_sf; // NVFP4 block scales [rows, K/16]
   int a_by_token;      // 1: A row = token of the sorted row (via perm); 0: A row = sorted row
   const int* perm;     // sorted row -> pair id (pair < P: token = pair / topk; else pair - P)
   int topk;
   int P;               // T * topk
-  const int* rowshift; // A_BF16: per A row, power-of-two shift applied when staging
-  const unsigned* rowmax;  // A_F32: per A row, bits of max |value|
+  const int* rowshift; // A_F16: per A row, the power-of-two shift of its fp16 copy (nullptr = 0)
   const float* gsa;    // activation global scale (nullptr = 1)
   // Outputs.
   float* h;            // [rows, I] fp32 (EPI_SWIGLU_F32)
@@ -93,20 +100,27 @@ struct PermuteArgs {
   int* perm;           // [P + T]
   int* inv;            // [P + T]
   int* glist;          // [E + 1]
-  int* gcount;         // [1]
+  int* gcount;         // [2]: non-empty groups, groups with > kBigGroupRows rows
   int32_t* offsets_out;  // optional copies
   int32_t* perm_out;
-  // row shifts of the bf16 activations (optional) and zeroing of a row-max buffer
+  // fp16 copy of the bf16 activations with per-row shifts (optional) and
+  // zeroing of a row-max buffer
   const uint16_t* x;   // [T, H] bf16 or nullptr
   int H;
   int* rowshift;       // [T]
+  f16* x16;            // [T, H]
   unsigned* zero_buf;  // [n_zero] set to 0, or nullptr
   int n_zero;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
-hipError_t launch_rowshift_bf16(const uint16_t* x, int rows, int cols, int* rowshift,
-                                hipStream_t stream);
+// fp16 copy of bf16 rows scaled by per-row powers of two (rowshift[r]).
+hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift, f16* x16,
+                              hipStream_t stream);
+// fp16 copy of the fp32 hidden rows [0, offsets[n_groups]) with per-row shifts
+// from their max |h| bits.
+hipError_t launch_h_to_f16(const float* h, const unsigned* hmax, const int* offsets, int end_index,
+                           int rows_max, int cols, f16* h16, int* hshift, hipStream_t stream);
 hipError_t launch_amax_to_gs(const unsigned* rowmax, int rows, float* gs_out, hipStream_t stream);
 
 struct CombineArgs {

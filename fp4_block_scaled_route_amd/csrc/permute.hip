@@ -30,8 +30,11 @@ constexpr int kPermWaves = 16;
 constexpr int kMaxExperts = 512;
 }  // namespace
 
-__device__ void rowshift_rows(const uint16_t* x, int rows, int cols, int* rowshift, int first_wave,
-                              int wave_stride) {
+// One wave per row: max |x| of the bf16 row, the power-of-two shift that maps
+// it into [2^14, 2^15), and the fp16 copy of the row scaled by that power of
+// two (exact: bf16 values have 8 significant bits), stored step-major.
+__device__ void rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift, f16* x16, int first_wave,
+                            int wave_stride) {
   const int lane = threadIdx.x & 63;
   for (int r = first_wave; r < rows; r += wave_stride) {
     const uint16_t* row = x + (int64_t)r * cols;
@@ -47,7 +50,20 @@ __device__ void rowshift_rows(const uint16_t* x, int rows, int cols, int* rowshi
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    if (lane == 0) rowshift[r] = shift_from_maxbits(mx << 16);
+    const int sh = shift_from_maxbits(mx << 16);
+    if (lane == 0) rowshift[r] = sh;
+    f16* out = x16 + (int64_t)r * cols;
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + c);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = (f16)__builtin_ldexpf(bf16_bits_to_float(u[e] & 0xFFFFu), sh);
+        o[2 * e + 1] = (f16)__builtin_ldexpf(bf16_bits_to_float(u[e] >> 16), sh);
+      }
+      *reinterpret_cast<f16x8*>(out + step_major_pos(c)) = o;
+    }
   }
 }
 
@@ -56,7 +72,7 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
     // row shifts of x and clearing of the row-max buffer
     const int nwav = (gridDim.x - 1) * (blockDim.x / 64);
     const int w = (blockIdx.x - 1) * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (a.x) rowshift_rows(a.x, a.T, a.H, a.rowshift, w, nwav);
+    if (a.x) rows_to_f16(a.x, a.T, a.H, a.rowshift, a.x16, w, nwav);
     if (a.zero_buf)
       for (int i = (blockIdx.x - 1) * blockDim.x + threadIdx.x; i < a.n_zero; i += (gridDim.x - 1) * blockDim.x)
         a.zero_buf[i] = 0u;
@@ -65,7 +81,6 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
 
   __shared__ int hist[kPermWaves][kMaxExperts];
   __shared__ int goff[kMaxExperts + 2];
-  __shared__ int wsum[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.T * a.topk;
@@ -175,17 +190,51 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
     a.glist[rank] = g;
   }
   if (tid < 64) {
-    int cnt = 0;
-    for (int g = lane; g < G; g += 64) cnt += (goff[g + 1] - goff[g]) > 0;
+    int cnt = 0, big = 0;
+    for (int g = lane; g < G; g += 64) {
+      const int mg = goff[g + 1] - goff[g];
+      cnt += mg > 0;
+      big += mg > kBigGroupRows;
+    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
-    if (lane == 0) *a.gcount = cnt;
+    for (int o = 32; o >= 1; o >>= 1) {
+      cnt += __shfl_xor(cnt, o);
+      big += __shfl_xor(big, o);
+    }
+    if (lane == 0) {
+      a.gcount[0] = cnt;
+      a.gcount[1] = big;
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void nvfp4_rowshift_bf16(const uint16_t* x, int rows, int cols, int* rowshift) {
+__global__ __launch_bounds__(256) void nvfp4_rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift,
+                                                         f16* x16) {
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  rowshift_rows(x, rows, cols, rowshift, w, gridDim.x * 4);
+  rows_to_f16(x, rows, cols, rowshift, x16, w, gridDim.x * 4);
+}
+
+// fp16 copy of the fp32 hidden rows with per-row shifts from max |h|, stored
+// step-major.
+__global__ __launch_bounds__(256) void nvfp4_h_to_f16(const float* h, const unsigned* hmax, const int* offsets,
+                                                      int end_index, int cols, f16* h16, int* hshift) {
+  const int rows = offsets[end_index];
+  const int lane = threadIdx.x & 63;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += gridDim.x * 4) {
+    const int sh = shift_from_maxbits(hmax[r]);
+    if (lane == 0) hshift[r] = sh;
+    const float* src = h + (int64_t)r * cols;
+    f16* dst = h16 + (int64_t)r * cols;
+    for (int c = lane * 8; c < cols; c += 64 * 8) {
+      const float4 v0 = *reinterpret_cast<const float4*>(src + c);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + c + 4);
+      const f16x8 o = {(f16)__builtin_ldexpf(v0.x, sh), (f16)__builtin_ldexpf(v0.y, sh),
+                       (f16)__builtin_ldexpf(v0.z, sh), (f16)__builtin_ldexpf(v0.w, sh),
+                       (f16)__builtin_ldexpf(v1.x, sh), (f16)__builtin_ldexpf(v1.y, sh),
+                       (f16)__builtin_ldexpf(v1.z, sh), (f16)__builtin_ldexpf(v1.w, sh)};
+      *reinterpret_cast<f16x8*>(dst + step_major_pos(c)) = o;
+    }
+  }
 }
 
 // gs = (max over rows of the row maxima) / 2688 for calibrating the global
@@ -210,7 +259,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   if (a.E > kMaxExperts) return hipErrorInvalidValue;
   int extra = 0;
   if (a.x || a.zero_buf) {
-    const int by_rows = a.x ? (a.T + 15) / 16 : 0;
+    const int by_rows = a.x ? (a.T + 15) / 16 : 0;   // 16 waves per block, one row each
     const int by_zero = a.zero_buf ? (a.n_zero + 1023) / 1024 : 0;
     extra = max(1, min(1024, max(by_rows, by_zero)));
   }
@@ -218,9 +267,16 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rowshift_bf16(const uint16_t* x, int rows, int cols, int* rowshift, hipStream_t s) {
-  const int grid = max(1, min(1024, (rows + 3) / 4));
-  hipLaunchKernelGGL(nvfp4_rowshift_bf16, dim3(grid), dim3(256), 0, s, x, rows, cols, rowshift);
+hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift, f16* x16, hipStream_t s) {
+  const int grid = max(1, min(2048, (rows + 3) / 4));
+  hipLaunchKernelGGL(nvfp4_rows_to_f16, dim3(grid), dim3(256), 0, s, x, rows, cols, rowshift, x16);
+  return hipGetLastError();
+}
+
+hipError_t launch_h_to_f16(const float* h, const unsigned* hmax, const int* offsets, int end_index, int rows_max,
+                           int cols, f16* h16, int* hshift, hipStream_t s) {
+  const int grid = max(1, min(2048, (rows_max + 3) / 4));
+  hipLaunchKernelGGL(nvfp4_h_to_f16, dim3(grid), dim3(256), 0, s, h, hmax, offsets, end_index, cols, h16, hshift);
   return hipGetLastError();
 }
 

@@ -108,11 +108,11 @@ def status_string(status: int) -> str:
 
 
 def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
-                 out: Optional[Sequence[torch.Tensor]] = None):
+                 out: Optional[Sequence[torch.Tensor]] = None, gs_out: Optional[torch.Tensor] = None):
     """NVFP4-quantize bf16 activations [M, K].  ``gs`` None: the global scale is
-    computed on the device (max|x| / 2688) and returned; otherwise ``gs`` (a
-    1-element fp32 device tensor) is used.  Returns (codes [M,K/2] u8,
-    scales [M,K/16] u8, gs [1] fp32)."""
+    computed on the device (max|x| / 2688) into ``gs_out`` (allocated if not
+    given) and returned; otherwise ``gs`` (a 1-element fp32 device tensor) is
+    used.  Returns (codes [M,K/2] u8, scales [M,K/16] u8, gs [1] fp32)."""
     m, k = x.shape
     if out is None:
         q = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
@@ -120,7 +120,10 @@ def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
     else:
         q, sf = out
     compute = gs is None
-    gsb = torch.empty(1, dtype=torch.float32, device=x.device) if compute else gs
+    if compute:
+        gsb = gs_out if gs_out is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        gsb = gs
     _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _stream()))
     return q, sf, gsb
 
