@@ -212,13 +212,16 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   const int n_big_max = std::min(G, Pt / (kBigGroupRows + 1));
   const double rows_per_group = (double)Pt / (double)G;
   const int maxc_big = rows_per_group > kBigGroupRows ? 8 : 4;
-  auto two_launches = [&](GemmArgs g, int amode, int epi, int r) -> bool {
+  // ev_big / ev_small: stage events recorded before each of the two launches
+  auto two_launches = [&](GemmArgs g, int amode, int epi, int r, int ev_big, int ev_small) -> bool {
     // the 8-chunk LDS kernel reuses each staged B fragment across 4 fragments
     GemmShape big{maxc_big, maxc_big >= 8 ? 4 : r}, small{1, r};
+    ev(ev_big);
     g.list_part = 0;
     g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, big) - 1) /
                  gemm_rows_per_block(epi, big));
     if (launch_gemm(g, amode, epi, big, n_big_max, s) != hipSuccess) return false;
+    ev(ev_small);
     g.list_part = 1;
     g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, small) - 1) /
                  gemm_rows_per_block(epi, small));
@@ -249,7 +252,6 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   if (launch_permute(pa, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
 
   // 2. gate/up GEMM with fused SwiGLU
-  ev(1);
   GemmArgs g1{};
   g1.w = a->w1;
   g1.w_sf = a->w1_sf;
@@ -281,12 +283,12 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g1.hq_sf = h_fp4 ? ws + L.hq_sf : nullptr;
   g1.h_gs = a->a2_gs;
   const int epi1 = h_fp4 ? EPI_SWIGLU_FP4 : EPI_SWIGLU_F32;
-  if (!two_launches(g1, fp4 ? A_FP4 : A_F16, epi1, 2)) return NVFP4_ERR_LAUNCH;
+  if (!two_launches(g1, fp4 ? A_FP4 : A_F16, epi1, 2, 1, 2)) return NVFP4_ERR_LAUNCH;
   if (!h_fp4 && a->a2_gs_out)
     if (launch_amax_to_gs(hmax, Pt, a->a2_gs_out, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
 
   // 3. fp16 copy of h (unless it is NVFP4), down GEMM scattering each pair's row
-  ev(2);
+  ev(3);
   int* hshift = h_fp4 ? nullptr : reinterpret_cast<int*>(ws + L.hshift);
   f16* h16 = h_fp4 ? nullptr : reinterpret_cast<f16*>(ws + L.h16);
   if (!h_fp4)
@@ -318,10 +320,10 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g2.rowshift = hshift;
   g2.gsa = h_fp4 ? a->a2_gs : nullptr;
   g2.slot = slot;
-  if (!two_launches(g2, h_fp4 ? A_FP4 : A_F16, EPI_SLOT, 2)) return NVFP4_ERR_LAUNCH;
+  if (!two_launches(g2, h_fp4 ? A_FP4 : A_F16, EPI_SLOT, 2, 4, 5)) return NVFP4_ERR_LAUNCH;
 
   // 4. weighted combine
-  ev(3);
+  ev(6);
   CombineArgs ca{};
   ca.slot = slot;
   ca.ids = a->topk_ids;
@@ -333,7 +335,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   ca.shared = S;
   ca.y = static_cast<uint16_t*>(a->y);
   if (launch_combine(ca, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
-  ev(4);
+  ev(7);
   return NVFP4_OK;
 }
 

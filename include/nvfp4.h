@@ -147,10 +147,14 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
  * y [T, H] bf16 output, fully overwritten.
  * workspace: nvfp4_moe_workspace_size(...) bytes of device scratch; h_fp4 = 1
  * sizes it for calls with a2_gs != NULL (smaller), 0 for a2_gs == NULL.
- * stage_events: optional host array of 5 hipEvent_t; event i is recorded on
- * `stream` before stage i (permute, gate/up GEMM, down GEMM, combine) and
- * event 4 after the last one (instrumentation for timing single kernels).
+ * stage_events: optional host array of NVFP4_MOE_STAGE_EVENTS hipEvent_t
+ * (instrumentation for timing single kernels), recorded on `stream`:
+ *   [0] permute [1] gate/up GEMM, groups of > 4 rows [2] gate/up GEMM, the
+ *   other groups [3] conversion of h (fp32 h only) [4] down GEMM, groups of
+ *   > 4 rows [5] down GEMM, the other groups [6] combine [7] end;
+ * event i is recorded before the work it names.
  */
+#define NVFP4_MOE_STAGE_EVENTS 8
 typedef struct nvfp4_moe_args {
   int64_t T, H, I, E, topk;
   const void* x;
