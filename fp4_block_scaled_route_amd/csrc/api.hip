@@ -211,11 +211,13 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   // most Pt / (kBigGroupRows + 1) groups can be that big.
   const int n_big_max = std::min(G, Pt / (kBigGroupRows + 1));
   const double rows_per_group = (double)Pt / (double)G;
-  const int maxc_big = rows_per_group > kBigGroupRows ? 8 : 4;
+  // big groups: 64-row passes on 4-wave workgroups (a few hot groups), or
+  // 112-row passes on 8-wave workgroups sharing one LDS tile (large batches)
+  const bool large_batch = rows_per_group > 16;
   // ev_big / ev_small: stage events recorded before each of the two launches
   auto two_launches = [&](GemmArgs g, int amode, int epi, int r, int ev_big, int ev_small) -> bool {
-    // the 8-chunk LDS kernel reuses each staged B fragment across 4 fragments
-    GemmShape big{maxc_big, maxc_big >= 8 ? 4 : r}, small{1, r};
+    GemmShape big = large_batch ? GemmShape{7, 4, 8} : GemmShape{4, r, 4};
+    GemmShape small{1, r, 4};
     ev(ev_big);
     g.list_part = 0;
     g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, big) - 1) /

@@ -123,7 +123,7 @@ __device__ __forceinline__ int shift_of(const GemmArgs& a, int arow) {
 // Weight fragments of this wave, read with buffer loads: one resource per
 // group (codes and scales), one 32-bit lane offset shared by all fragments,
 // and wave-uniform fragment offsets (scalar registers).
-template <int R, int EP>
+template <int R, int EP, int NW = kNW>
 struct Frags {
   int fbase[R];
   bool fvalid[R];
@@ -143,12 +143,12 @@ struct Frags {
     for (int f = 0; f < R; ++f) {
       int row0;
       if constexpr (is_swiglu<EP>()) {
-        const int gate = nbk * block_rows<R, kNW, EP>() + (wave * (R / 2) + (f >> 1)) * 16;
+        const int gate = nbk * block_rows<R, NW, EP>() + (wave * (R / 2) + (f >> 1)) * 16;
         fbase[f] = gate;
         fvalid[f] = gate < a.I;
         row0 = (f & 1 ? a.I : 0) + gate;
       } else {
-        const int base = nbk * block_rows<R, kNW, EP>() + (wave * R + f) * 16;
+        const int base = nbk * block_rows<R, NW, EP>() + (wave * R + f) * 16;
         fbase[f] = base;
         fvalid[f] = base < a.N;
         row0 = base;
@@ -204,8 +204,8 @@ __device__ __forceinline__ void transpose4(u32x4& v) {
 // Epilogue for one pass.  acc[f][c]: fragment f, token chunk c; lane holds
 // D rows 4*lg..4*lg+3 of the fragment for token row pbase + 16c + lr.
 // Rows at or past `mlim` (end of this pass) are not written.
-template <int R, int MAXC, int EP>
-__device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, const Frags<R, EP>& fr,
+template <int R, int MAXC, int EP, int NW>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, const Frags<R, EP, NW>& fr,
                                          f32x4 (&acc)[R][MAXC], int nc, int pbase, int mlim, int lr, int lg) {
   if constexpr (EP == EPI_Y_BF16 || EP == EPI_SLOT) {
 #pragma unroll
@@ -415,7 +415,7 @@ void nvfp4_gemm_compact(const GemmArgs a) {
         }
       }
     }
-    epilogue<R, 1, EP>(a, it, fr, acc, 1, pbase, pbase + prow, lr, lg);
+    epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, pbase + prow, lr, lg);
   }
 }
 
@@ -533,7 +533,7 @@ void nvfp4_gemm_direct(const GemmArgs a) {
       }
       fr.load(wb1, min(kc + 3, last));
     }
-    epilogue<R, 1, EP>(a, it, fr, acc, 1, pbase, min(it.m, pbase + 16), lr, lg);
+    epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, min(it.m, pbase + 16), lr, lg);
   }
 }
 
@@ -541,12 +541,12 @@ void nvfp4_gemm_direct(const GemmArgs a) {
 // LDS kernel: activation chunks staged per workgroup
 // ---------------------------------------------------------------------------
 
-template <int MAXC, int R, int AM, int EP>
-__global__ __launch_bounds__(kNW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
+template <int MAXC, int R, int NW, int AM, int EP>
+__global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   static_assert(!is_swiglu<EP>() || (R % 2 == 0), "SwiGLU needs gate/up fragment pairs");
   constexpr int PR = 16 * MAXC;         // activation rows per pass
   constexpr int TPR = 32;               // threads per staged row (8 elements each)
-  constexpr int RSTEP = kNW * 64 / TPR; // rows staged per thread sweep
+  constexpr int RSTEP = NW * 64 / TPR;  // rows staged per thread sweep
   constexpr int SROWS = (PR + RSTEP - 1) / RSTEP;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][PR * kLdsRow];
 
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kNW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   Item it;
   if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
   const int nbk = blockIdx.x % a.nb;
-  Frags<R, EP> fr;
+  Frags<R, EP, NW> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
   const int64_t KB = K / 2, KS = K / 16;
@@ -614,7 +614,11 @@ __global__ __launch_bounds__(kNW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) acc[f][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const WBuf<R>& wb, int buf) {
+    // Weights: one rolling buffer.  The first 16 bytes of every lane's codes
+    // (steps 0-3) are refilled with the next chunk's as soon as step 3 has
+    // decoded them, the second 16 bytes and the scale word after step 7.
+    WBuf<R> wb;
+    auto compute = [&](int buf, int next_kc) {
       f16 sc[R][4];
 #pragma unroll
       for (int f = 0; f < R; ++f) scales4(wb.s[f], sc[f]);
@@ -624,6 +628,17 @@ __global__ __launch_bounds__(kNW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         f16x8 af[R];
 #pragma unroll
         for (int f = 0; f < R; ++f) af[f] = decode8(word_of(wb.c0[f], wb.c1[f], q), sc[f][q >> 1]);
+        if (q == 3) {
+#pragma unroll
+          for (int f = 0; f < R; ++f) wb.c0[f] = buf_load16(fr.rw, fr.vw, fr.sw[f] + next_kc * 128);
+        }
+        if (q == 7) {
+#pragma unroll
+          for (int f = 0; f < R; ++f) {
+            wb.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
+            wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+          }
+        }
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
           if (c < nc) {
@@ -639,26 +654,24 @@ __global__ __launch_bounds__(kNW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       }
     };
 
-    WBuf<R> wb0, wb1;
-    fr.load(wb0, 0);
-    if (nkc > 1) fr.load(wb1, 1);
+    // chunks past the end re-read the last chunk (in bounds, unused)
+    const int last = nkc - 1;
+    fr.load(wb, 0);
     stage_load(0);
     stage_write(0);
     __syncthreads();
     for (int kc = 0; kc < nkc; kc += 2) {
       if (kc + 1 < nkc) stage_load(kc + 1);
-      compute(wb0, 0);
-      if (kc + 2 < nkc) fr.load(wb0, kc + 2);
+      compute(0, min(kc + 1, last));
       if (kc + 1 < nkc) stage_write(1);
       __syncthreads();
       if (kc + 1 >= nkc) break;
       if (kc + 2 < nkc) stage_load(kc + 2);
-      compute(wb1, 1);
-      if (kc + 3 < nkc) fr.load(wb1, kc + 3);
+      compute(1, min(kc + 2, last));
       if (kc + 2 < nkc) stage_write(0);
       __syncthreads();
     }
-    epilogue<R, MAXC, EP>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
+    epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
   }
 }
 
@@ -679,12 +692,17 @@ hipError_t launch_direct(const GemmArgs& a, int n_items, hipStream_t s) {
 }
 
 template <int AM, int EP, int R>
-hipError_t launch_lds(const GemmArgs& a, int maxc, int n_items, hipStream_t s) {
+hipError_t launch_lds(const GemmArgs& a, int maxc, int nw, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
+  if (nw == 8 && maxc == 7 && R == 4) {
+    hipLaunchKernelGGL((nvfp4_gemm_lds<7, R, 8, AM, EP>), dim3(n_items), dim3(8 * 64), 0, s, a);
+    return hipGetLastError();
+  }
+  if (nw != kNW) return hipErrorInvalidValue;
   switch (maxc) {
-    case 2: hipLaunchKernelGGL((nvfp4_gemm_lds<2, R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((nvfp4_gemm_lds<4, R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((nvfp4_gemm_lds<8, R, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((nvfp4_gemm_lds<2, R, kNW, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((nvfp4_gemm_lds<4, R, kNW, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((nvfp4_gemm_lds<8, R, kNW, AM, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -701,8 +719,8 @@ hipError_t dispatch(const GemmArgs& a, GemmShape sh, int n_groups, hipStream_t s
     }
   }
   switch (sh.r) {
-    case 2: return launch_lds<AM, EP, 2>(a, sh.maxc, n_items, s);
-    case 4: return launch_lds<AM, EP, 4>(a, sh.maxc, n_items, s);
+    case 2: return launch_lds<AM, EP, 2>(a, sh.maxc, sh.nw, n_items, s);
+    case 4: return launch_lds<AM, EP, 4>(a, sh.maxc, sh.nw, n_items, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -711,7 +729,7 @@ hipError_t dispatch(const GemmArgs& a, GemmShape sh, int n_groups, hipStream_t s
 
 int gemm_rows_per_block(int epi, GemmShape sh) {
   const bool sw = epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4;
-  return sw ? kNW * (sh.r / 2) * 16 : kNW * sh.r * 16;
+  return sw ? sh.nw * (sh.r / 2) * 16 : sh.nw * sh.r * 16;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, GemmShape sh, int n_groups, hipStream_t s) {

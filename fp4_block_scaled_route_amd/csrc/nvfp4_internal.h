@@ -84,8 +84,9 @@ struct GemmArgs {
 
 // Tile shape choice of one GEMM launch.
 struct GemmShape {
-  int maxc;   // token chunks of 16 per pass (1, 2, 4, 8)
+  int maxc;   // token chunks of 16 per pass (1 = barrier-free kernels; 2, 4, 7, 8 = LDS kernel)
   int r;      // 16-row weight fragments per wave
+  int nw = 4; // waves per workgroup
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, GemmShape shape, int n_groups,
