@@ -247,7 +247,7 @@ def run_moe(args, cfg):
         moe_step(cfg, st)
     torch.cuda.synchronize()
     hip = HipEvents()
-    NEV = 8
+    NEV = 8    # stage i runs from event i to event i + 1
     evs = [hip.create(NEV) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)

@@ -218,15 +218,14 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   auto two_launches = [&](GemmArgs g, int amode, int epi, int r, int ev_big, int ev_small) -> bool {
     GemmShape big = large_batch ? GemmShape{7, 4, 8} : GemmShape{4, r, 4};
     GemmShape small{1, r, 4};
+    const int half = epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1;
     ev(ev_big);
     g.list_part = 0;
-    g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, big) - 1) /
-                 gemm_rows_per_block(epi, big));
+    g.nb = (int)((g.N / half + gemm_rows_per_block(epi, big) - 1) / gemm_rows_per_block(epi, big));
     if (launch_gemm(g, amode, epi, big, n_big_max, s) != hipSuccess) return false;
     ev(ev_small);
     g.list_part = 1;
-    g.nb = (int)((g.N / (epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1) + gemm_rows_per_block(epi, small) - 1) /
-                 gemm_rows_per_block(epi, small));
+    g.nb = (int)((g.N / half + gemm_rows_per_block(epi, small) - 1) / gemm_rows_per_block(epi, small));
     return launch_gemm(g, amode, epi, small, G, s) == hipSuccess;
   };
 
@@ -286,11 +285,11 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g1.h_gs = a->a2_gs;
   const int epi1 = h_fp4 ? EPI_SWIGLU_FP4 : EPI_SWIGLU_F32;
   if (!two_launches(g1, fp4 ? A_FP4 : A_F16, epi1, 2, 1, 2)) return NVFP4_ERR_LAUNCH;
+
+  // 3. calibration and fp16 copy of h (unless it is NVFP4), down GEMM scattering each pair's row
+  ev(3);
   if (!h_fp4 && a->a2_gs_out)
     if (launch_amax_to_gs(hmax, Pt, a->a2_gs_out, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
-
-  // 3. fp16 copy of h (unless it is NVFP4), down GEMM scattering each pair's row
-  ev(3);
   int* hshift = h_fp4 ? nullptr : reinterpret_cast<int*>(ws + L.hshift);
   f16* h16 = h_fp4 ? nullptr : reinterpret_cast<f16*>(ws + L.h16);
   if (!h_fp4)

@@ -569,7 +569,7 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   for (int pass = 0; pass < npass; ++pass) {
     const int pbase = pass * PR;
     const int prow = min(PR, it.m - pbase);
-    const int nc = (prow + 15) >> 4;
+    const int nc = __builtin_amdgcn_readfirstlane((prow + 15) >> 4);
 
     int srow[SROWS];
     bool sval[SROWS];
@@ -616,39 +616,57 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
 
     // Weights: one rolling buffer.  The first 16 bytes of every lane's codes
     // (steps 0-3) are refilled with the next chunk's as soon as step 3 has
-    // decoded them, the second 16 bytes and the scale word after step 7.
+    // decoded them, the scale word at step 4 and the second 16 bytes after
+    // step 7.
     WBuf<R> wb;
+    // B fragments go through a one-deep software pipeline over the items
+    // (q, c) = (MFMA step, token chunk) with c < nc: the LDS read of the next
+    // item is issued before the MFMAs of the current one.  nc is uniform, so
+    // the choice of the next item is a scalar select.
+    const int lane_off = lr * kLdsRow + (AM == A_F16 ? lg * 16 : lg * 128);
+    auto item_off = [&](int q, int c) {
+      return c * 16 * kLdsRow + (AM == A_F16 ? q * 64 : q * 16);
+    };
     auto compute = [&](int buf, int next_kc) {
-      f16 sc[R][4];
+      // scale bytes 0-1 (steps 0-3) are converted now, bytes 2-3 at step 4,
+      // after which the scale word is refilled with the next chunk's: every
+      // weight load is issued four steps before its first use
+      f16x2 sc[R];
 #pragma unroll
-      for (int f = 0; f < R; ++f) scales4(wb.s[f], sc[f]);
-      const uint8_t* B = &lds[buf][0];
+      for (int f = 0; f < R; ++f) sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb.s[f], 1.0f, false);
+      const uint8_t* B = &lds[buf][0] + lane_off;
+      f16x8 bcur = *reinterpret_cast<const f16x8*>(B + item_off(0, 0));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
+        if (q == 4) {
+#pragma unroll
+          for (int f = 0; f < R; ++f) {
+            sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb.s[f], 1.0f, true);
+            wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+          }
+        }
         f16x8 af[R];
 #pragma unroll
-        for (int f = 0; f < R; ++f) af[f] = decode8(word_of(wb.c0[f], wb.c1[f], q), sc[f][q >> 1]);
+        for (int f = 0; f < R; ++f) af[f] = decode8(word_of(wb.c0[f], wb.c1[f], q), sc[f][(q >> 1) & 1]);
         if (q == 3) {
 #pragma unroll
           for (int f = 0; f < R; ++f) wb.c0[f] = buf_load16(fr.rw, fr.vw, fr.sw[f] + next_kc * 128);
         }
         if (q == 7) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) {
-            wb.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
-            wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
-          }
+          for (int f = 0; f < R; ++f) wb.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
         }
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
           if (c < nc) {
-            // fp16 rows are staged in their step-major order; NVFP4 rows are
-            // decoded into natural order
-            const int col = AM == A_F16 ? (4 * q + lg) * 16 : (64 * lg + 8 * q) * 2;
-            const f16x8 b = *reinterpret_cast<const f16x8*>(B + (16 * c + lr) * kLdsRow + col);
+            // next item: (q, c + 1) while c + 1 < nc, else (q + 1, 0); after
+            // the last item a harmless re-read of (0, 0)
+            const int noff = c + 1 < nc ? item_off(q, c + 1) : item_off(q < 7 ? q + 1 : 0, 0);
+            const f16x8 bnext = *reinterpret_cast<const f16x8*>(B + noff);
 #pragma unroll
             for (int f = 0; f < R; ++f)
-              acc[f][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], b, acc[f][c], 0, 0, 0);
+              acc[f][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], bcur, acc[f][c], 0, 0, 0);
+            bcur = bnext;
           }
         }
       }

@@ -27,10 +27,10 @@
  *
  * Pointers are DEVICE pointers unless marked "host".  `stream` is a
  * hipStream_t (NULL = the default stream).  Every call only enqueues work on
- * `stream` and returns; it never synchronises, never allocates or frees, and
- * keeps no state between calls (calls on different streams may run
- * concurrently as long as their buffers do not overlap).  The caller owns
- * every buffer.
+ * `stream` and returns; it never synchronises, never allocates or frees device
+ * memory, and keeps no state between calls (calls on different streams may
+ * run concurrently as long as their buffers do not overlap; a call can be
+ * captured into a HIP graph).  The caller owns every buffer.
  *
  * Constraints (checked on the host before any launch):
  *   K and every reduction length % 256 == 0; output widths % 16 == 0;
@@ -150,9 +150,10 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
  * stage_events: optional host array of NVFP4_MOE_STAGE_EVENTS hipEvent_t
  * (instrumentation for timing single kernels), recorded on `stream`:
  *   [0] permute [1] gate/up GEMM, groups of > 4 rows [2] gate/up GEMM, the
- *   other groups [3] conversion of h (fp32 h only) [4] down GEMM, groups of
- *   > 4 rows [5] down GEMM, the other groups [6] combine [7] end;
- * event i is recorded before the work it names.
+ *   other groups [3] calibration and conversion of h (fp32 h only) [4] down
+ *   GEMM, groups of > 4 rows [5] down GEMM, the other groups [6] combine
+ *   [7] end; event i is recorded before the work it names, so stage i lasts
+ *   from event i to event i + 1.
  */
 #define NVFP4_MOE_STAGE_EVENTS 8
 typedef struct nvfp4_moe_args {
