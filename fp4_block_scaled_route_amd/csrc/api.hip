@@ -205,7 +205,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   const int Pt = P + S * (int)T;
   const int G = (int)E + S;
   auto ev = [&](int i) {
-    if (a->stage_events) (void)hipEventRecord(static_cast<hipEvent_t>(a->stage_events[i]), s);
+    if (a->stage_events && a->stage_events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->stage_events[i]), s);
   };
   // Groups with more than kBigGroupRows rows run on the LDS-staged kernel; at
   // most Pt / (kBigGroupRows + 1) groups can be that big.

@@ -153,7 +153,8 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
  *   other groups [3] calibration and conversion of h (fp32 h only) [4] down
  *   GEMM, groups of > 4 rows [5] down GEMM, the other groups [6] combine
  *   [7] end; event i is recorded before the work it names, so stage i lasts
- *   from event i to event i + 1.
+ *   from event i to event i + 1.  NULL entries are skipped (each recorded
+ *   event costs a few microseconds between two kernels).
  */
 #define NVFP4_MOE_STAGE_EVENTS 8
 typedef struct nvfp4_moe_args {

@@ -99,5 +99,12 @@ def test_moe_stage_events_in_order():
         assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[i]),
                                        ctypes.c_void_p(evs[i + 1])) == 0
         assert ms.value >= 0.0, (i, ms.value)
+    # NULL entries are skipped: only the pair around the first gate/up launch
+    y2 = torch.empty_like(y)
+    ops.moe_grouped(**args, out=y2, stage_events=[0, evs[1], evs[2], 0, 0, 0, 0, 0])
+    torch.cuda.synchronize()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[1]), ctypes.c_void_p(evs[2])) == 0
+    assert ms.value >= 0.0
+    assert torch.equal(y, y2)
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
