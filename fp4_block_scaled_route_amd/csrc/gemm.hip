@@ -159,7 +159,7 @@ struct Frags {
     }
   }
 
-  // Codes only (scales come from load_scales4).
+  // Codes only (scales come from load_scales8).
   __device__ __forceinline__ void load_codes(u32x4 (&c0)[R], u32x4 (&c1)[R], int kc) const {
 #pragma unroll
     for (int f = 0; f < R; ++f) {
@@ -168,14 +168,19 @@ struct Frags {
     }
   }
 
-  // Scale words of 4 consecutive chunks [4*sc, 4*sc+4) with one 16-byte load
-  // per lane: lane group G loads the 16 scale bytes of chunk 4*sc+G of its row
-  // (chunk index clamped to the last chunk); transpose4 then hands every lane
-  // its own 4-byte word of each of the 4 chunks.
-  __device__ __forceinline__ void load_scales4(u32x4 (&raw)[R], int sc, int nkc, int lg) const {
-    const int kc = min(4 * sc + lg, nkc - 1);
+  // Scale words of 8 consecutive chunks [8*sc, 8*sc+8): lane group G loads
+  // the 16 scale bytes of chunks 8*sc+G and 8*sc+4+G of its row (clamped to
+  // the last chunk), both at once, so the row's 128 scale bytes of the group
+  // are requested together; transpose4 of raw[f][h] then gives every lane its
+  // word of chunks 8*sc+4h .. 8*sc+4h+3.
+  __device__ __forceinline__ void load_scales8(u32x4 (&raw)[R][2], int sc, int nkc, int lg) const {
+    const int k0 = min(8 * sc + lg, nkc - 1);
+    const int k1 = min(8 * sc + 4 + lg, nkc - 1);
 #pragma unroll
-    for (int f = 0; f < R; ++f) raw[f] = buf_load16(rs, vs - lg * 4 + kc * 16, ss[f]);
+    for (int f = 0; f < R; ++f) {
+      raw[f][0] = buf_load16(rs, vs - lg * 4 + k0 * 16, ss[f]);
+      raw[f][1] = buf_load16(rs, vs - lg * 4 + k1 * 16, ss[f]);
+    }
   }
 
   __device__ __forceinline__ void load(WBuf<R>& wb, int kc) const {
@@ -297,13 +302,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
 // ---------------------------------------------------------------------------
 //
 // Per 256-K chunk a wave issues 2 code loads per fragment, 1/4 scale load per
-// fragment (4 chunks of scales per load, transposed across lane groups) and
-// ceil(rows/2) activation loads: lanes 0-31 load 512 bytes of one row, lanes
-// 32-63 of the next.  The activation rows go through a wave-private LDS slot
-// (LDS operations of one wave complete in order, so no barrier is needed) and
-// are read back in the MFMA layout; lanes of absent rows read row 0 (their
-// columns are discarded).  Activations are loaded two chunks ahead, weights
-// two chunks ahead, scales one 4-chunk group ahead.
+// fragment (the scales of 8 chunks come with two loads per fragment issued
+// together, so each weight row's 128 scale bytes of the group are fetched
+// once; transposed across lane groups) and ceil(rows/2) activation loads:
+// lanes 0-31 load 512 bytes of one row, lanes 32-63 of the next.  The
+// activation rows go through a wave-private LDS slot (LDS operations of one
+// wave complete in order, so no barrier is needed) and are read back in the
+// MFMA layout; lanes of absent rows read row 0 (their columns are
+// discarded).  Activations are loaded two chunks ahead, weights two chunks
+// ahead, scales one 8-chunk group ahead.
 
 constexpr int kSmallRows = 4;
 constexpr int kSlotPitch = kChunk * 2 + 64;           // bytes per staged row (bank-shifted)
@@ -360,13 +367,13 @@ void nvfp4_gemm_compact(const GemmArgs a) {
     };
 
     u32x4 wc0a[R], wc1a[R], wc0b[R], wc1b[R];   // codes of two chunks in flight
-    u32x4 sraw[R];                              // scales of the next 4-chunk group
-    u32x4 scur[R];                              // this lane's scale word of each chunk of the group
+    u32x4 sraw[R][2];                           // scales of the next 8-chunk group
+    u32x4 scur[R][2];                           // this lane's scale word of each chunk of the group
 
-    auto compute = [&](const u32x4 (&c0)[R], const u32x4 (&c1)[R], const uint8_t* slot, int c4) {
+    auto compute = [&](const u32x4 (&c0)[R], const u32x4 (&c1)[R], const uint8_t* slot, int c8) {
       f16 sc[R][4];
 #pragma unroll
-      for (int f = 0; f < R; ++f) scales4(scur[f][c4], sc[f]);
+      for (int f = 0; f < R; ++f) scales4(scur[f][c8 >> 2][c8 & 3], sc[f]);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const f16x8 bf = *reinterpret_cast<const f16x8*>(slot + rd + q * 64);
@@ -380,7 +387,7 @@ void nvfp4_gemm_compact(const GemmArgs a) {
     };
 
     // prologue
-    fr.load_scales4(sraw, 0, nkc, lg);
+    fr.load_scales8(sraw, 0, nkc, lg);
     bload(bq0a, bq0b, 0);
     bload(bq1a, bq1b, min(1, last));
     fr.load_codes(wc0a, wc1a, 0);
@@ -388,27 +395,30 @@ void nvfp4_gemm_compact(const GemmArgs a) {
     bstore(slot0, bq0a, bq0b);
     bload(bq0a, bq0b, min(2, last));
 
-    // one iteration = one group of 4 chunks; chunk kc uses codes set (kc%2),
+    // one iteration = one group of 8 chunks; chunk kc uses codes set (kc%2),
     // activation slot (kc%2); at its end the activations of chunk kc+1 are
     // stored to slot ((kc+1)%2) and chunk kc+3 is requested
-    for (int kc = 0; kc < nkc; kc += 4) {
+    for (int kc = 0; kc < nkc; kc += 8) {
 #pragma unroll
       for (int f = 0; f < R; ++f) {
-        scur[f] = sraw[f];
-        transpose4(scur[f]);
-      }
-      fr.load_scales4(sraw, kc / 4 + 1, nkc, lg);
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int k = kc + c4;
+        for (int h = 0; h < 2; ++h) {
+          scur[f][h] = sraw[f][h];
+          transpose4(scur[f][h]);
+        }
+      }
+      fr.load_scales8(sraw, kc / 8 + 1, nkc, lg);
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) {
+        const int k = kc + c8;
         if (k >= nkc) break;
-        if ((c4 & 1) == 0) {
-          compute(wc0a, wc1a, slot0, c4);
+        if ((c8 & 1) == 0) {
+          compute(wc0a, wc1a, slot0, c8);
           fr.load_codes(wc0a, wc1a, min(k + 2, last));
           bstore(slot1, bq1a, bq1b);
           bload(bq1a, bq1b, min(k + 3, last));
         } else {
-          compute(wc0b, wc1b, slot1, c4);
+          compute(wc0b, wc1b, slot1, c8);
           fr.load_codes(wc0b, wc1b, min(k + 2, last));
           bstore(slot0, bq0a, bq0b);
           bload(bq0a, bq0b, min(k + 3, last));
@@ -730,11 +740,10 @@ template <int AM, int EP>
 hipError_t dispatch(const GemmArgs& a, GemmShape sh, int n_groups, hipStream_t s) {
   const int n_items = n_groups * a.nb;
   if (sh.maxc == 1) {
-    switch (sh.r) {
-      case 2: return launch_direct<AM, EP, 2>(a, n_items, s);
-      case 4: return launch_direct<AM, EP, 4>(a, n_items, s);
-      default: return hipErrorInvalidValue;
-    }
+    // barrier-free kernels: 2 fragments per wave (4 would not fit the
+    // register budget of 4 waves per SIMD)
+    if (sh.r != 2) return hipErrorInvalidValue;
+    return launch_direct<AM, EP, 2>(a, n_items, s);
   }
   switch (sh.r) {
     case 2: return launch_lds<AM, EP, 2>(a, sh.maxc, sh.nw, n_items, s);
