@@ -626,9 +626,18 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
 
     // Weights: one rolling buffer.  The first 16 bytes of every lane's codes
     // (steps 0-3) are refilled with the next chunk's as soon as step 3 has
-    // decoded them, the scale word at step 4 and the second 16 bytes after
-    // step 7.
+    // decoded them, the second 16 bytes after step 7, the scale word at step 4.
+    // Large-batch configuration (PAIR): scale words go by pairs of chunks
+    // (wb.s: even chunk, s_odd: odd chunk), both requested at step 4 of the odd
+    // chunk, so the 32 scale bytes of a row and pair come with one fetch of
+    // their line (per-chunk requests, 3 us apart, refetch the line each time
+    // under this kernel's streaming load).  Measured on MI355X: pairs cut the
+    // fully-FP4 gate/up GEMM's HBM traffic from 1.9x to 1.55x its algorithmic
+    // bytes, but slow the 4-wave configuration (few workgroups per CU, latency
+    // bound) down, which keeps per-chunk scale words.
+    constexpr bool PAIR = NW == 8;
     WBuf<R> wb;
+    uint32_t s_odd[R];
     // B fragments go through a one-deep software pipeline over the items
     // (q, c) = (MFMA step, token chunk) with c < nc: the LDS read of the next
     // item is issued before the MFMAs of the current one.  nc is uniform, so
@@ -637,22 +646,31 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     auto item_off = [&](int q, int c) {
       return c * 16 * kLdsRow + (AM == A_F16 ? q * 64 : q * 16);
     };
+    // buf: LDS buffer = parity of the chunk; next_kc: chunk whose codes and
+    // scales (PAIR: for an odd chunk, with those of next_kc + 1) are requested
     auto compute = [&](int buf, int next_kc) {
-      // scale bytes 0-1 (steps 0-3) are converted now, bytes 2-3 at step 4,
-      // after which the scale word is refilled with the next chunk's: every
-      // weight load is issued four steps before its first use
+      // scale bytes 0-1 (steps 0-3) are converted now, bytes 2-3 at step 4
       f16x2 sc[R];
 #pragma unroll
-      for (int f = 0; f < R; ++f) sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb.s[f], 1.0f, false);
+      for (int f = 0; f < R; ++f)
+        sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : wb.s[f], 1.0f, false);
       const uint8_t* B = &lds[buf][0] + lane_off;
       f16x8 bcur = *reinterpret_cast<const f16x8*>(B + item_off(0, 0));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (q == 4) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) {
-            sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb.s[f], 1.0f, true);
-            wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+          for (int f = 0; f < R; ++f)
+            sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : wb.s[f], 1.0f, true);
+          if (!PAIR) {
+#pragma unroll
+            for (int f = 0; f < R; ++f) wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+          } else if (buf == 1) {
+#pragma unroll
+            for (int f = 0; f < R; ++f) {
+              wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+              s_odd[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + min(next_kc + 1, nkc - 1) * 16);
+            }
           }
         }
         f16x8 af[R];
@@ -685,6 +703,10 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     // chunks past the end re-read the last chunk (in bounds, unused)
     const int last = nkc - 1;
     fr.load(wb, 0);
+    if constexpr (PAIR) {
+#pragma unroll
+      for (int f = 0; f < R; ++f) s_odd[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + min(1, last) * 16);
+    }
     stage_load(0);
     stage_write(0);
     __syncthreads();
