@@ -55,7 +55,7 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, i
     L.h16 = take(sizeof(uint16_t) * (size_t)Pt * I);
     L.hq = L.hq_sf = 0;
   }
-  L.slot = take(sizeof(float) * (size_t)Pt * H);
+  L.slot = take(sizeof(uint16_t) * (size_t)Pt * H);
   L.total = off;
   return L;
 }
@@ -199,7 +199,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   int* rowshift = reinterpret_cast<int*>(ws + L.rowshift);
   f16* x16 = reinterpret_cast<f16*>(ws + L.x16);
   unsigned* hmax = reinterpret_cast<unsigned*>(ws + L.hmax);
-  float* slot = reinterpret_cast<float*>(ws + L.slot);
+  uint16_t* slot = reinterpret_cast<uint16_t*>(ws + L.slot);
   const int S = has_shared ? 1 : 0;
   const int P = (int)(T * k);
   const int Pt = P + S * (int)T;

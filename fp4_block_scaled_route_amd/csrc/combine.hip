@@ -2,9 +2,10 @@
 // (gfx950).  For token t: y_t = sum_{j=0..topk-1} w[t, j] * o(t, j) + o_shared(t),
 // accumulated in fp32 in that fixed order, then rounded to bf16.  o(t, j) is
 // the down-projection row of pair t*topk + j, already scaled by the pair's
-// weight_scale_2; routing weights are applied here, after the down GEMM (the
-// "weighted combine" of the MoE layer; summation order is a reading).  A pair
-// whose expert id is outside [0, E) contributes nothing.
+// weight_scale_2 and stored in bf16 (the layer's output precision); routing
+// weights are applied here, after the down GEMM (the "weighted combine" of the
+// MoE layer; summation order is a reading).  A pair whose expert id is outside
+// [0, E) contributes nothing.
 #include "device_util.h"
 
 namespace nvfp4 {
@@ -19,16 +20,22 @@ __global__ __launch_bounds__(256) void nvfp4_moe_combine(const CombineArgs a) {
     const int id = a.ids[t * a.topk + j];
     if (id < 0 || id >= a.E) continue;
     const float w = a.w[t * a.topk + j];
-    const float4* src = reinterpret_cast<const float4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n);
-    const float4 v0 = src[0], v1 = src[1];
-    acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
-    acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+    const uint4 v = *reinterpret_cast<const uint4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += w * bf16_bits_to_float(u[i] & 0xffffu);
+      acc[2 * i + 1] += w * bf16_bits_to_float(u[i] >> 16);
+    }
   }
   if (a.shared) {
-    const float4* src = reinterpret_cast<const float4*>(a.slot + (int64_t)(P + t) * a.H + n);
-    const float4 v0 = src[0], v1 = src[1];
-    acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
-    acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    const uint4 v = *reinterpret_cast<const uint4*>(a.slot + (int64_t)(P + t) * a.H + n);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_bits_to_float(u[i] & 0xffffu);
+      acc[2 * i + 1] += bf16_bits_to_float(u[i] >> 16);
+    }
   }
   uint4 o;
   o.x = float_to_bf16_bits(acc[0]) | (float_to_bf16_bits(acc[1]) << 16);

@@ -226,14 +226,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh) * it.alpha;
+        uint2 o;
+        o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+        o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
         if constexpr (EP == EPI_Y_BF16) {
-          uint2 o;
-          o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
-          o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
           *reinterpret_cast<uint2*>(a.y + (int64_t)r * a.N + n0) = o;
         } else {
           const int pid = a.perm[r];
-          *reinterpret_cast<float4*>(a.slot + (int64_t)pid * a.N + n0) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<uint2*>(a.slot + (int64_t)pid * a.N + n0) = o;
         }
       }
     }

@@ -34,7 +34,7 @@ enum EpiMode {
   EPI_Y_BF16 = 0,      // y[row, n] = bf16(alpha * acc)                    (dense linear)
   EPI_SWIGLU_F32 = 1,  // h[row, i] = silu(alpha*gate) * (alpha*up), fp32, + row max |h|
   EPI_SWIGLU_FP4 = 2,  // same h, quantized to NVFP4 with a supplied global scale
-  EPI_SLOT = 3         // slot[pair, n] = alpha * acc, fp32                (down GEMM)
+  EPI_SLOT = 3         // slot[pair, n] = bf16(alpha * acc)                (down GEMM)
 };
 
 struct GemmArgs {
@@ -78,7 +78,7 @@ struct GemmArgs {
   uint8_t* hq;         // [rows, I/2] (EPI_SWIGLU_FP4)
   uint8_t* hq_sf;      // [rows, I/16]
   const float* h_gs;   // global scale used to quantize h (EPI_SWIGLU_FP4)
-  float* slot;         // [pairs, N] (EPI_SLOT), row = perm[sorted row]
+  uint16_t* slot;      // [pairs, N] bf16 (EPI_SLOT), row = perm[sorted row]
   uint16_t* y;         // [M, N] bf16 (EPI_Y_BF16)
 };
 
@@ -125,7 +125,7 @@ hipError_t launch_h_to_f16(const float* h, const unsigned* hmax, const int* offs
 hipError_t launch_amax_to_gs(const unsigned* rowmax, int rows, float* gs_out, hipStream_t stream);
 
 struct CombineArgs {
-  const float* slot;    // [P + T, H]
+  const uint16_t* slot; // [P + T, H] bf16
   const int32_t* ids;   // [T, topk]
   const float* w;       // [T, topk]
   int T, topk, E, H, shared;
