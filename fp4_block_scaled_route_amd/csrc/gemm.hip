@@ -638,10 +638,6 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     constexpr bool PAIR = NW == 8;
     WBuf<R> wb;
     uint32_t s_odd[R];
-    // B fragments go through a one-deep software pipeline over the items
-    // (q, c) = (MFMA step, token chunk) with c < nc: the LDS read of the next
-    // item is issued before the MFMAs of the current one.  nc is uniform, so
-    // the choice of the next item is a scalar select.
     const int lane_off = lr * kLdsRow + (AM == A_F16 ? lg * 16 : lg * 128);
     auto item_off = [&](int q, int c) {
       return c * 16 * kLdsRow + (AM == A_F16 ? q * 64 : q * 16);
@@ -655,7 +651,6 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       for (int f = 0; f < R; ++f)
         sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : wb.s[f], 1.0f, false);
       const uint8_t* B = &lds[buf][0] + lane_off;
-      f16x8 bcur = *reinterpret_cast<const f16x8*>(B + item_off(0, 0));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (q == 4) {
@@ -687,14 +682,10 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
           if (c < nc) {
-            // next item: (q, c + 1) while c + 1 < nc, else (q + 1, 0); after
-            // the last item a harmless re-read of (0, 0)
-            const int noff = c + 1 < nc ? item_off(q, c + 1) : item_off(q < 7 ? q + 1 : 0, 0);
-            const f16x8 bnext = *reinterpret_cast<const f16x8*>(B + noff);
+            const f16x8 b = *reinterpret_cast<const f16x8*>(B + item_off(q, c));
 #pragma unroll
             for (int f = 0; f < R; ++f)
-              acc[f][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], bcur, acc[f][c], 0, 0, 0);
-            bcur = bnext;
+              acc[f][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], b, acc[f][c], 0, 0, 0);
           }
         }
       }
