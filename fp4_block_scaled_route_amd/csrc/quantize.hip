@@ -18,20 +18,37 @@ namespace nvfp4 {
 
 __global__ void nvfp4_quant_zero(float* gs) { gs[0] = 0.0f; }
 
+// Grid-wide max |x|: every thread folds 4 independent 16-byte loads per
+// iteration, the block reduces through LDS, and one atomic per block (not per
+// wave: thousands of atomics on one word serialise) merges the blocks.
 __global__ __launch_bounds__(256) void nvfp4_quant_amax(const uint16_t* x, int64_t n8, float* amax_word) {
+  const uint4* v4 = reinterpret_cast<const uint4*>(x);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   uint32_t mx = 0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+  auto fold = [&](const uint4 v) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       mx = max(mx, u[e] & 0x7FFFu);
       mx = max(mx, (u[e] >> 16) & 0x7FFFu);
     }
+  };
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    const uint4 a = v4[i], b = v4[i + stride], c = v4[i + 2 * stride], d = v4[i + 3 * stride];
+    fold(a);
+    fold(b);
+    fold(c);
+    fold(d);
   }
+  for (; i < n8; i += stride) fold(v4[i]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned*>(amax_word), mx << 16);
+  __shared__ uint32_t wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(reinterpret_cast<unsigned*>(amax_word), max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16);
 }
 
 // one thread per 16-element block
@@ -78,7 +95,7 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, float* g
   if (compute_gs) {
     hipLaunchKernelGGL(nvfp4_quant_zero, dim3(1), dim3(1), 0, s, gs);
     const int64_t n8 = n / 8;
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(2048, (n8 + 255) / 256));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
     hipLaunchKernelGGL(nvfp4_quant_amax, dim3(grid), dim3(256), 0, s, x, n8, gs);
   }
   if (nblk > 0) {
