@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+BF16_RIDGE_FLOP_PER_BYTE = FP16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # 312.5
 BYTES_PER_EXPERT_W1 = 2 * 2048 * 7168 // 2 + 2 * 2048 * 7168 // 16       # 16,515,072
 BYTES_PER_EXPERT_W2 = 7168 * 2048 // 2 + 7168 * 2048 // 16               # 8,257,536
 FLOPS_PER_PAIR = 2 * (2 * 2048 * 7168 + 7168 * 2048)                     # 88,080,384
@@ -41,6 +42,9 @@ WORKLOADS = {
     "moe_prefill": dict(kind="moe", T=128, H=7168, I=2048, E=384, k=8, routing="zipf", shared=True, fp4=False),
     # fully FP4 path: 4096 tokens, both GEMMs on NVFP4 activations, no shared expert
     "moe_fp4": dict(kind="moe", T=4096, H=7168, I=2048, E=384, k=8, routing="uniform", shared=False, fp4=True),
+    # router gate (FP8 round-tripped bf16 weight, top-8 softmax) at the decode and large-batch token counts
+    "router_decode": dict(kind="router", T=64, H=7168, E=384, k=8),
+    "router_4096": dict(kind="router", T=4096, H=7168, E=384, k=8),
     # dense NVFP4 linear at projection shapes
     "linear_q_a_m1": dict(kind="linear", M=1, N=1536, K=7168),
     "linear_q_a_m128": dict(kind="linear", M=128, N=1536, K=7168),
@@ -395,6 +399,83 @@ def run_linear(args, cfg):
     }
 
 
+def run_router(args, cfg):
+    """Router gate: logits of T tokens against the FP8 round-tripped weight,
+    then top-k softmax (one nvfp4_router_topk call: the logits GEMM and the
+    selection)."""
+    import numpy as np
+    import torch
+
+    from fp4_block_scaled_route_amd import ops, synth
+
+    t, h, e, k = cfg["T"], cfg["H"], cfg["E"], cfg["k"]
+    x = synth.bf16_normal((t, h), args.seed).cuda()
+    w = synth.router_weight(e, h, args.seed)
+    w_bytes = e * h * 2
+    copies = max(1, int(np.ceil(1.0e9 / w_bytes)))   # rotate weights past the last-level cache
+    w_rt, _ = ops.router_prepare(w.cuda())
+    wrs = [w_rt.clone() for _ in range(copies)]
+    logits = torch.empty((t, e), dtype=torch.float32, device="cuda")
+    ids = torch.empty((t, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((t, k), dtype=torch.float32, device="cuda")
+    work = torch.empty(max(1, ops.router_workspace_size(t, h, e)), dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        ops.router_topk(x, wrs[i % copies], k, logits, ids, wts, work)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        ops.router_topk(x, wrs[i % copies], k, logits, ids, wts, work)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # algorithmic: weight + activations read, logits written, selection written
+    nbytes = w_bytes + t * h * 2 + t * e * 4 + t * k * 8
+    flops = 2 * t * e * h
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfl = flops / (ms * 1e-3) / 1e12
+    bound_mfma = flops / nbytes > BF16_RIDGE_FLOP_PER_BYTE
+    if bound_mfma:
+        roof = dict(bound="mfma", achieved=round(tfl, 2), peak=FP16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tfl / FP16_PEAK_TFLOPS, 4), traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
+    roof.update(kernel="nvfp4_router_logits + nvfp4_router_select (one call)", kernel_ms=round(ms, 5),
+                algorithmic_bytes_per_launch=nbytes, algorithmic_flops_per_launch=flops)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import router
+        log("timing the CPU oracle on a bounded sample ...")
+        _, _, wr_ref = router.router_weight_roundtrip(w.float().numpy())
+        xs = synth.bf16_to_float64(x[:16].cpu())
+        t_start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t_start < 10.0:
+            router.route(xs, wr_ref, k)
+            reps += 1
+        sec = (time.perf_counter() - t_start) / reps
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        sample_bytes = w_bytes + 16 * h * 2 + 16 * e * 4 + 16 * k * 8
+        cpu = dict(value=round(sample_bytes / sec / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                   sample=f"16 tokens against the whole weight, float64 numpy oracle, {reps} repetitions in "
+                          f"about 10 s")
+    return {
+        "metric": "router gate GB/s or TFLOP/s (%roofline), 1xMI355X",
+        "value": round(gbs if not bound_mfma else tfl, 3), "unit": "GB/s" if not bound_mfma else "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"router gate: {t} tokens x hidden {h}, {e} experts, top-{k} softmax, FP8 "
+                               f"round-tripped bf16 weight, {copies} rotating weight copies",
+                   "name": args.workload},
+        "tflops": round(tfl, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
 def run_copy(args):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE readings to bytes."""
@@ -435,7 +516,8 @@ def main():
         run_copy(args)
         return
     cfg = WORKLOADS[args.workload]
-    res = run_moe(args, cfg) if cfg["kind"] == "moe" else run_linear(args, cfg)
+    run = {"moe": run_moe, "linear": run_linear, "router": run_router}[cfg["kind"]]
+    res = run(args, cfg)
     print(json.dumps(res), flush=True)
 
 

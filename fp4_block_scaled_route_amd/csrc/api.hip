@@ -92,6 +92,40 @@ int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int 
                                            x_sf, static_cast<hipStream_t>(stream)));
 }
 
+int nvfp4_router_prepare(const void* w_bf16, int64_t E, int64_t H, float* scale, void* w_rt_bf16, void* stream) {
+  if (E <= 0 || H <= 0 || H % 256 != 0 || E >= kMaxDim || H >= kMaxDim || E * H >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (!w_bf16 || !scale || !w_rt_bf16) return NVFP4_ERR_NULL;
+  if (!aligned(w_bf16, 16) || !aligned(w_rt_bf16, 16) || !aligned(scale, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* w = static_cast<const uint16_t*>(w_bf16);
+  if (launch_bf16_amax(w, E * H, scale, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  return launch_status(launch_router_prepare(w, E * H, scale, static_cast<uint16_t*>(w_rt_bf16), s));
+}
+
+size_t nvfp4_router_workspace_size(int64_t T, int64_t H, int64_t E) {
+  if (T <= 0 || H <= 0 || E <= 0 || H % 256 != 0 || T >= kMaxDim || E > 512) return 0;
+  return sizeof(float) * (size_t)router_ksplit((int)T, (int)H, (int)E) * T * E;
+}
+
+int nvfp4_router_topk(const void* x_bf16, const void* w_rt_bf16, int64_t T, int64_t H, int64_t E, int64_t topk,
+                      float* logits, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (T < 0 || H <= 0 || H % 256 != 0 || E <= 0 || E > 512 || topk <= 0 || topk > E || topk > 64)
+    return NVFP4_ERR_SHAPE;
+  if (T >= kMaxDim || H >= kMaxDim || T * H * 2 >= kMaxBuffer || E * H * 2 >= kMaxBuffer || T * E >= kMaxDim)
+    return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!x_bf16 || !w_rt_bf16 || !logits || !topk_ids || !topk_w) return NVFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w_rt_bf16, 16) || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return NVFP4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < nvfp4_router_workspace_size(T, H, E)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  return launch_status(launch_router_topk(static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w_rt_bf16),
+                                          (int)T, (int)H, (int)E, (int)topk, logits, topk_ids, topk_w,
+                                          static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
 size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   (void)N;
   if (M <= 0 || K <= 0) return 0;

@@ -133,6 +133,21 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+// word = max |x| over n bf16 values (n % 8 == 0), as a float (zeroed first).
+hipError_t launch_bf16_amax(const uint16_t* x, int64_t n, float* word, hipStream_t stream);
+
+// Router gate (page P1, note on the router gate).  Prepare: scale = amax(w)/448,
+// w_rt = bf16(E4M3(RNE(w / scale)) * scale) over n elements; `scale` holds
+// amax on entry (from launch_bf16_amax) and amax/448 on exit.
+hipError_t launch_router_prepare(const uint16_t* w, int64_t n, float* scale, uint16_t* w_rt, hipStream_t stream);
+// logits[t, e] = sum_k x[t, k] * w_rt[e, k] (fp32 accumulate: K splits of
+// router_ksplit(T, H, E) partial sums in part [ks, T, E], added in split
+// order), then per token the top-k (descending, ties to the lower id) and the
+// softmax of the k values.
+int router_ksplit(int T, int H, int E);
+hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_rt, int T, int H, int E, int topk, float* logits,
+                              int32_t* ids, float* wts, float* part, hipStream_t stream);
+
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, float* gs, int compute_gs,
                                uint8_t* q, uint8_t* sf, hipStream_t stream);
 

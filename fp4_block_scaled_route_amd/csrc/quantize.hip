@@ -88,6 +88,16 @@ __global__ __launch_bounds__(256) void nvfp4_quant_blocks(const uint16_t* x, int
 
 __global__ void nvfp4_quant_finish(float* gs) { gs[0] = gs[0] / 2688.0f; }
 
+hipError_t launch_bf16_amax(const uint16_t* x, int64_t n, float* word, hipStream_t s) {
+  hipLaunchKernelGGL(nvfp4_quant_zero, dim3(1), dim3(1), 0, s, word);
+  const int64_t n8 = n / 8;
+  if (n8 > 0) {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
+    hipLaunchKernelGGL(nvfp4_quant_amax, dim3(grid), dim3(256), 0, s, x, n8, word);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, float* gs, int compute_gs, uint8_t* q,
                                uint8_t* sf, hipStream_t s) {
   const int64_t n = M * K;

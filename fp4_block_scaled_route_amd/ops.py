@@ -27,6 +27,9 @@ EXPORTED = (
     "nvfp4_linear",
     "nvfp4_moe_workspace_size",
     "nvfp4_moe_grouped",
+    "nvfp4_router_prepare",
+    "nvfp4_router_workspace_size",
+    "nvfp4_router_topk",
 )
 ABI_VERSION = 1
 
@@ -81,6 +84,13 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
         L.nvfp4_moe_grouped.restype = ctypes.c_int
         L.nvfp4_moe_grouped.argtypes = [ctypes.POINTER(MoeArgs), _c_ptr]
+        L.nvfp4_router_prepare.restype = ctypes.c_int
+        L.nvfp4_router_prepare.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]
+        L.nvfp4_router_workspace_size.restype = ctypes.c_size_t
+        L.nvfp4_router_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64]
+        L.nvfp4_router_topk.restype = ctypes.c_int
+        L.nvfp4_router_topk.argtypes = [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                        _c_ptr, ctypes.c_size_t, _c_ptr]
         if L.nvfp4_abi_version() != ABI_VERSION:
             raise RuntimeError("libnvfp4.so ABI version does not match the binding")
         _lib = L
@@ -194,3 +204,37 @@ def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
         a.stage_events = ctypes.cast(arr, ctypes.POINTER(_c_ptr))
     _check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream()))
     return y
+
+
+def router_prepare(w: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   scale_out: Optional[torch.Tensor] = None):
+    """FP8-E4M3 round trip of a bf16 router weight [E, H] (see
+    nvfp4_router_prepare).  Returns (w_rt bf16 [E, H], scale fp32 [1])."""
+    e, h = w.shape
+    w_rt = out if out is not None else torch.empty_like(w)
+    scale = scale_out if scale_out is not None else torch.empty(1, dtype=torch.float32, device=w.device)
+    _check(lib().nvfp4_router_prepare(_p(w), e, h, _p(scale), _p(w_rt), _stream()))
+    return w_rt, scale
+
+
+def router_workspace_size(t: int, h: int, e: int) -> int:
+    return int(lib().nvfp4_router_workspace_size(t, h, e))
+
+
+def router_topk(x: torch.Tensor, w_rt: torch.Tensor, topk: int, logits: Optional[torch.Tensor] = None,
+                ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """Router logits and top-k softmax (see nvfp4_router_topk).
+    Returns (logits fp32 [T, E], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    t, h = x.shape
+    e = w_rt.shape[0]
+    dev = x.device
+    logits = logits if logits is not None else torch.empty((t, e), dtype=torch.float32, device=dev)
+    ids = ids if ids is not None else torch.empty((t, topk), dtype=torch.int32, device=dev)
+    weights = weights if weights is not None else torch.empty((t, topk), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, router_workspace_size(t, h, e)), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().nvfp4_router_topk(_p(x), _p(w_rt), t, h, e, topk, _p(logits), _p(ids), _p(weights),
+                                   _p(workspace), wsb, _stream()))
+    return logits, ids, weights

@@ -37,6 +37,7 @@ import torch
 # stream tags
 _TAG_X, _TAG_W, _TAG_SF, _TAG_WS2, _TAG_ROUTE, _TAG_PERM = 1, 2, 3, 4, 5, 6
 _TAG_W1, _TAG_W1SF, _TAG_W2, _TAG_W2SF = 11, 12, 13, 14
+_TAG_ROUTER = 21
 _SHARED = 1 << 20   # expert index used for the shared expert's streams
 
 
@@ -178,6 +179,13 @@ def make_moe(t: int, h: int, i: int, e: int, k: int, seed: int = 0, routing: str
     sh = make_experts(1, h, i, seed, _SHARED, threads=threads) if shared else None
     return MoEInputs(x=x, topk_ids=ids, topk_w=w, experts=experts, shared=sh,
                      dims=dict(T=t, H=h, I=i, E=e, topk=k, routing=routing))
+
+
+def router_weight(e: int, h: int, seed: int, std: float = 0.05) -> torch.Tensor:
+    """Router gate weight [E, H] in bf16: N(0, std^2) (a stand-in for a
+    checkpoint's router weight, which is not available)."""
+    w = _rng(seed, _TAG_ROUTER).standard_normal((e, h), dtype=np.float32) * np.float32(std)
+    return torch.from_numpy(w).to(torch.bfloat16)
 
 
 def bf16_to_float64(x: torch.Tensor) -> np.ndarray:

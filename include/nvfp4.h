@@ -191,6 +191,39 @@ size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int6
                                 int has_shared, int h_fp4);
 int nvfp4_moe_grouped(const nvfp4_moe_args* args, void* stream);
 
+/*
+ * Router gate (page "commit 1121cd7 - single_shot_inference.py", note on the
+ * router gate): the router weight goes through an FP8-E4M3 round trip with one
+ * per-tensor scale amax/448 and back to bf16; the router is a plain linear of
+ * the activations with it, followed by top-k softmax routing.  Its outputs
+ * topk_ids / topk_w are exactly the routing inputs of nvfp4_moe_grouped.
+ *
+ * nvfp4_router_prepare - the weight preparation (done once per weight):
+ *   w_bf16     [E, H] bf16 router weight (already dequantized to bf16).
+ *   scale      device fp32 scalar, output: amax / 448.
+ *   w_rt_bf16  [E, H] bf16 output: bf16(E4M3(RNE(w / scale)) * scale), each
+ *              step one IEEE fp32 operation, E4M3 saturating at 448 with the
+ *              sign of w; scale == 0 gives zeros.
+ *   Requires H % 256 == 0.
+ *
+ * nvfp4_router_topk - logits and selection for T tokens:
+ *   x_bf16     [T, H] bf16 activations; w_rt_bf16 [E, H] from nvfp4_router_prepare.
+ *   logits     [T, E] fp32 output: sum_k x[t,k] * w_rt[e,k] (exact products,
+ *              fp32 accumulation in a fixed order for given T, H, E).
+ *   topk_ids   [T, topk] int32 output: experts by descending logit, ties to
+ *              the lower id.
+ *   topk_w     [T, topk] fp32 output: softmax of the topk selected logits.
+ *   workspace  device scratch of nvfp4_router_workspace_size(T, H, E) bytes
+ *              (partial sums of the K splits); contents undefined afterwards.
+ *   Requires H % 256 == 0, E <= 512, topk <= min(E, 64).  NaN logits are not
+ *   handled.
+ */
+int nvfp4_router_prepare(const void* w_bf16, int64_t E, int64_t H, float* scale, void* w_rt_bf16, void* stream);
+size_t nvfp4_router_workspace_size(int64_t T, int64_t H, int64_t E);
+int nvfp4_router_topk(const void* x_bf16, const void* w_rt_bf16, int64_t T, int64_t H, int64_t E, int64_t topk,
+                      float* logits, int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -101,3 +101,30 @@ def test_moe_validation(lib):
     assert base(a2_gs=FAKE, a2_gs_out=FAKE) == -6
     assert base(workspace_bytes=ws - 1) == -4
     assert base(y=ctypes.c_void_p(0x1008)) == -3
+
+
+def test_router_validation(lib):
+    L = lib
+    mis = ctypes.c_void_p(0x1002)
+    assert L.nvfp4_router_prepare(FAKE, 384, 200, FAKE, FAKE, None) == -2     # H not a multiple of 256
+    assert L.nvfp4_router_prepare(FAKE, 0, 256, FAKE, FAKE, None) == -2
+    assert L.nvfp4_router_prepare(None, 384, 256, FAKE, FAKE, None) == -1
+    assert L.nvfp4_router_prepare(mis, 384, 256, FAKE, FAKE, None) == -3
+
+    def topk(**kw):
+        a = dict(x=FAKE, w=FAKE, T=64, H=7168, E=384, k=8, lg=FAKE, ids=FAKE, wt=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return L.nvfp4_router_topk(a["x"], a["w"], a["T"], a["H"], a["E"], a["k"], a["lg"], a["ids"], a["wt"],
+                                   a["ws"], a["wsb"], None)
+    assert topk(E=513) == -2                 # more experts than the selection kernel holds
+    assert topk(k=0) == -2
+    assert topk(k=65) == -2
+    assert topk(E=4, k=5) == -2
+    assert topk(H=100) == -2
+    assert topk(T=0) == 0                    # nothing to do
+    assert topk(ids=None) == -1
+    assert topk(lg=ctypes.c_void_p(0x1001)) == -3
+    need = L.nvfp4_router_workspace_size(64, 7168, 384)
+    assert need > 0
+    assert topk(wsb=need - 1) == -4
+    assert topk(ws=None) == -4
