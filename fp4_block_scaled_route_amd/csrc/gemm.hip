@@ -76,6 +76,8 @@ template <int R, int NW, int EP>
 constexpr int block_rows() { return is_swiglu<EP>() ? NW * (R / 2) * 16 : NW * R * 16; }
 
 constexpr int kNW = 4;  // waves per workgroup
+// s_waitcnt operand (gfx9 encoding) waiting for all vector memory loads only
+constexpr int kVmcnt0 = 0x0F70;
 
 // Resolved work item.
 struct Item {
@@ -555,10 +557,24 @@ template <int MAXC, int R, int NW, int AM, int EP>
 __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   static_assert(!is_swiglu<EP>() || (R % 2 == 0), "SwiGLU needs gate/up fragment pairs");
   constexpr int PR = 16 * MAXC;         // activation rows per pass
-  constexpr int TPR = 32;               // threads per staged row (8 elements each)
-  constexpr int RSTEP = NW * 64 / TPR;  // rows staged per thread sweep
+  // Staging of the activation chunk, branch-free (rows of the pass past its
+  // last row read through an offset beyond the buffer and are not used).
+  //  fp16 rows: 32 threads per row, 16 bytes each; lanes 0-31 and 32-63 of a
+  //    wave take two rows.
+  //  NVFP4 rows: 4 threads per row, each 64 codes (32 bytes) and their 4 scale
+  //    bytes, decoded to 128 bytes of fp16; lane l of wave w takes row
+  //    16w + l%16, quarter l/16, so 8 consecutive lanes write 8 rows (distinct
+  //    LDS banks).
+  constexpr int TPR = AM == A_F16 ? 32 : 4;   // threads per staged row
+  constexpr int RSTEP = NW * 64 / TPR;        // rows staged per sweep of the workgroup
   constexpr int SROWS = (PR + RSTEP - 1) / RSTEP;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][PR * kLdsRow];
+  // four-wave configuration: the weights of two chunks in registers
+  constexpr bool DB = NW == 4;
+  // B fragments of a whole step read at once (see compute)
+  constexpr bool BQ = !(NW == 8 && AM == A_F16);
+  // every thread writes its rows (the rows past PR hold zeros nobody reads),
+  // so no wave-dependent branch separates the loads from their uses
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][SROWS * RSTEP * kLdsRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -570,10 +586,13 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   Frags<R, EP, NW> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
-  const int64_t KB = K / 2, KS = K / 16;
   const int nkc = K / kChunk;
-  const int seg = tid % TPR;
-  const int rsub = tid / TPR;
+  const int last = nkc - 1;
+  const int seg = AM == A_F16 ? lane & 31 : lg;
+  const int rsub = AM == A_F16 ? 2 * wave + (lane >> 5) : 16 * wave + lr;
+  const rsrc_t ra = make_rsrc(a.a, AM == A_F16 ? (uint32_t)a.a_rows * K * 2 : (uint32_t)a.a_rows * (K / 2));
+  const rsrc_t ras = make_rsrc(a.a_sf, AM == A_F16 ? 0u : (uint32_t)a.a_rows * (K / 16));
+  constexpr uint32_t kOut = 0x80000000u;
 
   const int npass = (it.m + PR - 1) / PR;
   for (int pass = 0; pass < npass; ++pass) {
@@ -581,40 +600,59 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     const int prow = min(PR, it.m - pbase);
     const int nc = __builtin_amdgcn_readfirstlane((prow + 15) >> 4);
 
-    int srow[SROWS];
-    bool sval[SROWS];
+    uint32_t so[SROWS], sso[SROWS];   // per-row offsets of codes (or fp16) and scales
 #pragma unroll
     for (int i = 0; i < SROWS; ++i) {
       const int rr = rsub + RSTEP * i;
-      sval[i] = rr < prow;
-      srow[i] = sval[i] ? a_row_of(a, it.row0 + pbase + rr) : 0;
+      const bool ok = rr < prow;   // (prow <= PR, so rows of the workgroup past PR load nothing)
+      const uint32_t arow = ok ? (uint32_t)a_row_of(a, it.row0 + pbase + rr) : 0u;
+      if constexpr (AM == A_F16) {
+        so[i] = ok ? arow * (uint32_t)K * 2 + seg * 16 : kOut;
+        sso[i] = 0;
+      } else {
+        so[i] = ok ? arow * (uint32_t)(K / 2) + seg * 32 : kOut;
+        sso[i] = ok ? arow * (uint32_t)(K / 16) + seg * 4 : kOut;
+      }
     }
-    u32x4 st0[SROWS];
-    uint32_t stc[SROWS], sts[SROWS];
+    u32x4 st0[SROWS], st1[SROWS];
+    uint32_t sts[SROWS];
+    // Only the sweeps holding rows of the pass (workgroup-uniform count) are
+    // written.  Four-wave configuration: only they load, too.  Eight-wave
+    // configuration (one sweep): every lane loads (absent rows read zeros
+    // without a memory access).
+    const int nsw = __builtin_amdgcn_readfirstlane((prow + RSTEP - 1) / RSTEP);
 
     auto stage_load = [&](int kc) {
 #pragma unroll
       for (int i = 0; i < SROWS; ++i) {
-        if (!sval[i]) continue;
+        if (DB && i >= nsw) break;
         if constexpr (AM == A_F16) {
-          st0[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.a) +
-                                                   ((int64_t)srow[i] * K + kc * kChunk + seg * 8) * 2);
+          st0[i] = buf_load16(ra, so[i], kc * kChunk * 2);
         } else {
-          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.a) + (int64_t)srow[i] * KB + kc * 128 + seg * 4;
-          stc[i] = *reinterpret_cast<const uint32_t*>(src);
-          sts[i] = a.a_sf[(int64_t)srow[i] * KS + kc * 16 + (seg >> 1)];
+          st0[i] = buf_load16(ra, so[i], kc * 128);
+          st1[i] = buf_load16(ra, so[i], kc * 128 + 16);
+          sts[i] = buf_load4(ras, sso[i], kc * 16);
         }
       }
     };
     auto stage_write = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < SROWS; ++i) {
-        if (!sval[i]) continue;
+        if (i >= nsw) break;
         const int rr = rsub + RSTEP * i;
-        f16x8 v;
-        if constexpr (AM == A_F16) v = __builtin_bit_cast(f16x8, st0[i]);
-        else v = decode8(stc[i], (f16)e4m3_to_float(sts[i]));
-        *reinterpret_cast<f16x8*>(&lds[buf][rr * kLdsRow + seg * 16]) = v;
+        if constexpr (AM == A_F16) {
+          *reinterpret_cast<u32x4*>(&lds[buf][rr * kLdsRow + seg * 16]) = st0[i];
+        } else {
+          const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sts[i], 1.0f, false);
+          const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sts[i], 1.0f, true);
+          uint8_t* dst = &lds[buf][rr * kLdsRow + seg * 128];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t w = j < 4 ? st0[i][j] : st1[i][j - 4];
+            const f16 sc = j < 2 ? s01[0] : j < 4 ? s01[1] : j < 6 ? s23[0] : s23[1];
+            *reinterpret_cast<f16x8*>(dst + j * 16) = decode8(w, sc);
+          }
+        }
       }
     };
 
@@ -636,53 +674,68 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     // bytes, but slow the 4-wave configuration (few workgroups per CU, latency
     // bound) down, which keeps per-chunk scale words.
     constexpr bool PAIR = NW == 8;
-    WBuf<R> wb;
+    WBuf<R> wb, wb1;
     uint32_t s_odd[R];
     const int lane_off = lr * kLdsRow + (AM == A_F16 ? lg * 16 : lg * 128);
     auto item_off = [&](int q, int c) {
       return c * 16 * kLdsRow + (AM == A_F16 ? q * 64 : q * 16);
     };
-    // buf: LDS buffer = parity of the chunk; next_kc: chunk whose codes and
-    // scales (PAIR: for an odd chunk, with those of next_kc + 1) are requested
-    auto compute = [&](int buf, int next_kc) {
+    // buf: LDS buffer = parity of the chunk; w: its weights; next_kc: chunk
+    // whose codes and scales (PAIR: for an odd chunk, with those of
+    // next_kc + 1) are requested into w while it is consumed (rolling buffer;
+    // the double-buffered configuration requests nothing here)
+    auto compute = [&](int buf, WBuf<R>& w, int next_kc) {
       // scale bytes 0-1 (steps 0-3) are converted now, bytes 2-3 at step 4
       f16x2 sc[R];
 #pragma unroll
       for (int f = 0; f < R; ++f)
-        sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : wb.s[f], 1.0f, false);
+        sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : w.s[f], 1.0f, false);
       const uint8_t* B = &lds[buf][0] + lane_off;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (q == 4) {
 #pragma unroll
           for (int f = 0; f < R; ++f)
-            sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : wb.s[f], 1.0f, true);
-          if (!PAIR) {
+            sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : w.s[f], 1.0f, true);
+          if (DB) {
+          } else if (!PAIR) {
 #pragma unroll
-            for (int f = 0; f < R; ++f) wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+            for (int f = 0; f < R; ++f) w.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
           } else if (buf == 1) {
 #pragma unroll
             for (int f = 0; f < R; ++f) {
-              wb.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
+              w.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
               s_odd[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + min(next_kc + 1, nkc - 1) * 16);
             }
           }
         }
+        // B fragments of every token chunk of the step, read before the
+        // decode so that the LDS latency hides behind it (chunks past the
+        // pass hold rows nobody uses; reading them keeps the number of LDS
+        // reads in flight the same on every path).  The eight-wave
+        // configuration with fp16 activations has no registers to spare and
+        // reads each fragment just before its MFMAs.
+        f16x8 bq[MAXC];
+        if constexpr (BQ) {
+#pragma unroll
+          for (int c = 0; c < MAXC; ++c) bq[c] = *reinterpret_cast<const f16x8*>(B + item_off(q, c));
+          __builtin_amdgcn_sched_barrier(0);
+        }
         f16x8 af[R];
 #pragma unroll
-        for (int f = 0; f < R; ++f) af[f] = decode8(word_of(wb.c0[f], wb.c1[f], q), sc[f][(q >> 1) & 1]);
-        if (q == 3) {
+        for (int f = 0; f < R; ++f) af[f] = decode8(word_of(w.c0[f], w.c1[f], q), sc[f][(q >> 1) & 1]);
+        if (!DB && q == 3) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) wb.c0[f] = buf_load16(fr.rw, fr.vw, fr.sw[f] + next_kc * 128);
+          for (int f = 0; f < R; ++f) w.c0[f] = buf_load16(fr.rw, fr.vw, fr.sw[f] + next_kc * 128);
         }
-        if (q == 7) {
+        if (!DB && q == 7) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) wb.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
+          for (int f = 0; f < R; ++f) w.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
         }
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
           if (c < nc) {
-            const f16x8 b = *reinterpret_cast<const f16x8*>(B + item_off(q, c));
+            const f16x8 b = BQ ? bq[c] : *reinterpret_cast<const f16x8*>(B + item_off(q, c));
 #pragma unroll
             for (int f = 0; f < R; ++f)
               acc[f][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], b, acc[f][c], 0, 0, 0);
@@ -692,7 +745,6 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     };
 
     // chunks past the end re-read the last chunk (in bounds, unused)
-    const int last = nkc - 1;
     fr.load(wb, 0);
     if constexpr (PAIR) {
 #pragma unroll
@@ -701,17 +753,39 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     stage_load(0);
     stage_write(0);
     __syncthreads();
-    for (int kc = 0; kc < nkc; kc += 2) {
-      if (kc + 1 < nkc) stage_load(kc + 1);
-      compute(0, min(kc + 1, last));
-      if (kc + 1 < nkc) stage_write(1);
+    // Pairs of chunks (even chunk in LDS buffer 0, odd in buffer 1), every
+    // half staging the next chunk (the last one again past the end: in
+    // bounds, into the buffer no wave reads any more); an odd last chunk runs
+    // after the loop.  Double-buffered configuration: each half starts by
+    // waiting for every load in flight (its own weights, requested a chunk
+    // earlier), then requests the next chunk's activations and weights, so
+    // the compiler's waits never cover loads that were just issued.
+    int kc = 0;
+    for (; kc + 1 < nkc; kc += 2) {
+      if constexpr (DB) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        stage_load(kc + 1);
+        fr.load(wb1, kc + 1);
+        compute(0, wb, kc + 1);
+      } else {
+        stage_load(kc + 1);
+        compute(0, wb, kc + 1);
+      }
+      stage_write(1);
       __syncthreads();
-      if (kc + 1 >= nkc) break;
-      if (kc + 2 < nkc) stage_load(kc + 2);
-      compute(1, min(kc + 2, last));
-      if (kc + 2 < nkc) stage_write(0);
+      if constexpr (DB) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        stage_load(min(kc + 2, last));
+        fr.load(wb, min(kc + 2, last));
+        compute(1, wb1, min(kc + 2, last));
+      } else {
+        stage_load(min(kc + 2, last));
+        compute(1, wb, min(kc + 2, last));
+      }
+      stage_write(0);
       __syncthreads();
     }
+    if (kc < nkc) compute(0, wb, last);
     epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
   }
 }
