@@ -250,7 +250,8 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   const bool large_batch = rows_per_group > 16;
   // ev_big / ev_small: stage events recorded before each of the two launches
   auto two_launches = [&](GemmArgs g, int amode, int epi, int r, int ev_big, int ev_small) -> bool {
-    GemmShape big = large_batch ? GemmShape{7, 4, 8} : GemmShape{4, r, 4};
+    // (the 8-wave configuration walks K in quads of 256-element chunks)
+    GemmShape big = !large_batch ? GemmShape{4, r, 4} : g.K % 1024 == 0 ? GemmShape{7, 4, 8} : GemmShape{8, r, 4};
     GemmShape small{1, r, 4};
     const int half = epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1;
     ev(ev_big);

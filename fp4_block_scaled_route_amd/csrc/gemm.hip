@@ -580,9 +580,23 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
+  // Eight-wave configuration: workgroups go to the 8 XCDs in turn (workgroup
+  // b to XCD b % 8); XCD x takes groups x, x + 8, ... with all nb row blocks
+  // of a group one after another, so the workgroups that read one group's
+  // activation rows run together on one XCD and share its L2.  (The grid is
+  // a multiple of 8 * nb.)  Four-wave configuration (a few groups): item =
+  // b / nb, spread over all XCDs.
+  int gi, nbk;
+  if constexpr (NW == 8) {
+    const int j = blockIdx.x >> 3;
+    gi = (j / a.nb) * 8 + (blockIdx.x & 7);
+    nbk = j % a.nb;
+  } else {
+    gi = blockIdx.x / a.nb;
+    nbk = blockIdx.x % a.nb;
+  }
   Item it;
-  if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
-  const int nbk = blockIdx.x % a.nb;
+  if (!resolve_item(a, gi, it)) return;
   Frags<R, EP, NW> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
@@ -662,52 +676,62 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) acc[f][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Weights: one rolling buffer.  The first 16 bytes of every lane's codes
-    // (steps 0-3) are refilled with the next chunk's as soon as step 3 has
-    // decoded them, the second 16 bytes after step 7, the scale word at step 4.
-    // Large-batch configuration (PAIR): scale words go by pairs of chunks
-    // (wb.s: even chunk, s_odd: odd chunk), both requested at step 4 of the odd
-    // chunk, so the 32 scale bytes of a row and pair come with one fetch of
-    // their line (per-chunk requests, 3 us apart, refetch the line each time
-    // under this kernel's streaming load).  Measured on MI355X: pairs cut the
-    // fully-FP4 gate/up GEMM's HBM traffic from 1.9x to 1.55x its algorithmic
-    // bytes, but slow the 4-wave configuration (few workgroups per CU, latency
-    // bound) down, which keeps per-chunk scale words.
-    constexpr bool PAIR = NW == 8;
+    // Weights.  Four-wave configuration (DB): the codes and scale words of
+    // two chunks in registers (wb, wb1), requested a whole chunk ahead.
+    // Eight-wave configuration (QUAD, no registers for that): one rolling
+    // buffer of codes, whose first 16 bytes per lane (steps 0-3) are refilled
+    // with the next chunk's once step 3 has decoded them and the second 16
+    // bytes after step 7; scale words by quads of chunks: lane group G loads
+    // the 16 scale bytes of chunk 4j + G of its row (all four groups' words of
+    // that chunk), and a 4x4 transpose across the lane groups gives every lane
+    // its word of the quad's four chunks.  A row's 64 scale bytes of a quad
+    // thus come with one request: requests per chunk or per pair of chunks,
+    // a few microseconds apart, fetched the 128-byte line again each time
+    // under this kernel's streaming load (measured on MI355X: 1.9x and 1.55x
+    // the algorithmic bytes of the fully-FP4 gate/up GEMM).
+    constexpr bool QUAD = NW == 8;
     WBuf<R> wb, wb1;
-    uint32_t s_odd[R];
+    u32x4 sq[R];        // QUAD: scale words of the quad (raw, then transposed)
+    uint32_t s3[R];     // QUAD: word of the quad's last chunk, while sq receives the next quad
+    auto load_quad = [&](int j) {   // raw scale bytes of quad j (chunks clamped to the last one)
+      const int k = min(4 * j + lg, last);
+#pragma unroll
+      for (int f = 0; f < R; ++f) sq[f] = buf_load16(fr.rs, fr.vs - lg * 4 + k * 16, fr.ss[f]);
+    };
     const int lane_off = lr * kLdsRow + (AM == A_F16 ? lg * 16 : lg * 128);
     auto item_off = [&](int q, int c) {
       return c * 16 * kLdsRow + (AM == A_F16 ? q * 64 : q * 16);
     };
     // buf: LDS buffer = parity of the chunk; w: its weights; next_kc: chunk
-    // whose codes and scales (PAIR: for an odd chunk, with those of
-    // next_kc + 1) are requested into w while it is consumed (rolling buffer;
-    // the double-buffered configuration requests nothing here)
-    auto compute = [&](int buf, WBuf<R>& w, int next_kc) {
+    // whose codes are requested into w while it is consumed (QUAD); j:
+    // position of the chunk in its quad (QUAD)
+    auto compute = [&](int buf, WBuf<R>& w, int next_kc, int j) {
+      if constexpr (QUAD) {
+        if (j == 0) {
+#pragma unroll
+          for (int f = 0; f < R; ++f) transpose4(sq[f]);
+        } else if (j == 3) {
+          // the next quad's raw words go to sq, a chunk before they are needed
+#pragma unroll
+          for (int f = 0; f < R; ++f) s3[f] = sq[f][3];
+          load_quad(next_kc / 4);
+          __builtin_amdgcn_sched_barrier(0);   // keep the requests here, a chunk ahead
+        }
+      }
+      auto sword = [&](int f) -> uint32_t {
+        if constexpr (QUAD) return j == 3 ? s3[f] : sq[f][j & 3];
+        else return w.s[f];
+      };
       // scale bytes 0-1 (steps 0-3) are converted now, bytes 2-3 at step 4
       f16x2 sc[R];
 #pragma unroll
-      for (int f = 0; f < R; ++f)
-        sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : w.s[f], 1.0f, false);
+      for (int f = 0; f < R; ++f) sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sword(f), 1.0f, false);
       const uint8_t* B = &lds[buf][0] + lane_off;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (q == 4) {
 #pragma unroll
-          for (int f = 0; f < R; ++f)
-            sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(PAIR && buf == 1 ? s_odd[f] : w.s[f], 1.0f, true);
-          if (DB) {
-          } else if (!PAIR) {
-#pragma unroll
-            for (int f = 0; f < R; ++f) w.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
-          } else if (buf == 1) {
-#pragma unroll
-            for (int f = 0; f < R; ++f) {
-              w.s[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + next_kc * 16);
-              s_odd[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + min(next_kc + 1, nkc - 1) * 16);
-            }
-          }
+          for (int f = 0; f < R; ++f) sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sword(f), 1.0f, true);
         }
         // B fragments of every token chunk of the step, read before the
         // decode so that the LDS latency hides behind it (chunks past the
@@ -724,11 +748,11 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         f16x8 af[R];
 #pragma unroll
         for (int f = 0; f < R; ++f) af[f] = decode8(word_of(w.c0[f], w.c1[f], q), sc[f][(q >> 1) & 1]);
-        if (!DB && q == 3) {
+        if (QUAD && q == 3) {
 #pragma unroll
           for (int f = 0; f < R; ++f) w.c0[f] = buf_load16(fr.rw, fr.vw, fr.sw[f] + next_kc * 128);
         }
-        if (!DB && q == 7) {
+        if (QUAD && q == 7) {
 #pragma unroll
           for (int f = 0; f < R; ++f) w.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
         }
@@ -745,47 +769,62 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     };
 
     // chunks past the end re-read the last chunk (in bounds, unused)
-    fr.load(wb, 0);
-    if constexpr (PAIR) {
-#pragma unroll
-      for (int f = 0; f < R; ++f) s_odd[f] = buf_load4(fr.rs, fr.vs, fr.ss[f] + min(1, last) * 16);
+    if constexpr (QUAD) {
+      fr.load_codes(wb.c0, wb.c1, 0);
+      load_quad(0);
+    } else {
+      fr.load(wb, 0);
     }
     stage_load(0);
     stage_write(0);
     __syncthreads();
-    // Pairs of chunks (even chunk in LDS buffer 0, odd in buffer 1), every
-    // half staging the next chunk (the last one again past the end: in
-    // bounds, into the buffer no wave reads any more); an odd last chunk runs
-    // after the loop.  Double-buffered configuration: each half starts by
-    // waiting for every load in flight (its own weights, requested a chunk
-    // earlier), then requests the next chunk's activations and weights, so
-    // the compiler's waits never cover loads that were just issued.
-    int kc = 0;
-    for (; kc + 1 < nkc; kc += 2) {
-      if constexpr (DB) {
+    // Even chunks in LDS buffer 0, odd ones in buffer 1; every chunk stages
+    // the next one (the last one again past the end: in bounds, into the
+    // buffer no wave reads any more).
+    if constexpr (QUAD) {
+      // quads of chunks (the host uses this configuration when 4 divides
+      // the chunk count)
+      for (int kc = 0; kc < nkc; kc += 4) {
+        stage_load(kc + 1);
+        compute(0, wb, kc + 1, 0);
+        stage_write(1);
+        __syncthreads();
+        stage_load(kc + 2);
+        compute(1, wb, kc + 2, 1);
+        stage_write(0);
+        __syncthreads();
+        stage_load(kc + 3);
+        compute(0, wb, kc + 3, 2);
+        stage_write(1);
+        __syncthreads();
+        stage_load(min(kc + 4, last));
+        compute(1, wb, min(kc + 4, last), 3);
+        stage_write(0);
+        __syncthreads();
+      }
+    } else {
+      // pairs of chunks; an odd last chunk runs after the loop.  Each half
+      // starts by waiting for every load in flight (its own weights,
+      // requested a chunk earlier), then requests the next chunk's
+      // activations and weights, so the compiler's waits never cover loads
+      // that were just issued.
+      int kc = 0;
+      for (; kc + 1 < nkc; kc += 2) {
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
         stage_load(kc + 1);
         fr.load(wb1, kc + 1);
-        compute(0, wb, kc + 1);
-      } else {
-        stage_load(kc + 1);
-        compute(0, wb, kc + 1);
-      }
-      stage_write(1);
-      __syncthreads();
-      if constexpr (DB) {
+        compute(0, wb, kc + 1, 0);
+        stage_write(1);
+        __syncthreads();
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
         stage_load(min(kc + 2, last));
         fr.load(wb, min(kc + 2, last));
-        compute(1, wb1, min(kc + 2, last));
-      } else {
-        stage_load(min(kc + 2, last));
-        compute(1, wb, min(kc + 2, last));
+        compute(1, wb1, min(kc + 2, last), 0);
+        stage_write(0);
+        __syncthreads();
       }
-      stage_write(0);
-      __syncthreads();
+      if (kc < nkc) compute(0, wb, last, 0);
     }
-    if (kc < nkc) compute(0, wb, last);
     epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
   }
 }
@@ -810,7 +849,11 @@ template <int AM, int EP, int R>
 hipError_t launch_lds(const GemmArgs& a, int maxc, int nw, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   if (nw == 8 && maxc == 7 && R == 4) {
-    hipLaunchKernelGGL((nvfp4_gemm_lds<7, R, 8, AM, EP>), dim3(n_items), dim3(8 * 64), 0, s, a);
+    if (a.K % (4 * kChunk) != 0) return hipErrorInvalidValue;   // quads of chunks
+    // whole rounds of 8 groups (see the XCD order in the kernel)
+    const int n_groups = n_items / a.nb;
+    const int grid = (n_groups + 7) / 8 * 8 * a.nb;
+    hipLaunchKernelGGL((nvfp4_gemm_lds<7, R, 8, AM, EP>), dim3(grid), dim3(8 * 64), 0, s, a);
     return hipGetLastError();
   }
   if (nw != kNW) return hipErrorInvalidValue;
