@@ -38,6 +38,7 @@ import torch
 _TAG_X, _TAG_W, _TAG_SF, _TAG_WS2, _TAG_ROUTE, _TAG_PERM = 1, 2, 3, 4, 5, 6
 _TAG_W1, _TAG_W1SF, _TAG_W2, _TAG_W2SF = 11, 12, 13, 14
 _TAG_ROUTER = 21
+_TAG_GL_X, _TAG_GL_W, _TAG_GL_SF, _TAG_GL_WS2 = 31, 32, 33, 34
 _SHARED = 1 << 20   # expert index used for the shared expert's streams
 
 
@@ -84,6 +85,32 @@ def make_linear(m: int, n: int, k: int, seed: int = 0, ws2: float = 0.002,
     w = random_bytes((n, k // 2), seed, _TAG_W)
     sf = e4m3_scales((n, k // 16), seed, _TAG_SF, 0, *sf_range)
     return LinearInputs(x=x, w=w, w_sf=sf, ws2=float(np.float32(ws2)))
+
+
+# ---------------------------------------------------------------------------
+# grouped linear (attention output projection wo_a)
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class GroupedLinearInputs:
+    x: torch.Tensor          # [T, G, K] bf16 (CPU)
+    w: np.ndarray            # [G, N, K/2] uint8
+    w_sf: np.ndarray         # [G, N, K/16] uint8
+    ws2: np.ndarray          # [G] float32
+
+
+def make_grouped_linear(t: int, g: int, n: int, k: int, seed: int = 0, sf_range=(0.01, 1.0)) -> GroupedLinearInputs:
+    """x ~ N(0,1) bf16; uniform codes; block scales U[0.01, 1] -> E4M3;
+    per-group weight_scale_2 ~ U[0.001, 0.003] (so that a group mix-up shows)."""
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    x = bf16_normal((t, g, k), seed, _TAG_GL_X)
+    w = np.stack([random_bytes((n, k // 2), seed, _TAG_GL_W, i) for i in range(g)])
+    sf = np.stack([e4m3_scales((n, k // 16), seed, _TAG_GL_SF, i, *sf_range) for i in range(g)])
+    ws2 = (_rng(seed, _TAG_GL_WS2).random(size=g, dtype=np.float32) * np.float32(0.002)
+           + np.float32(0.001)).astype(np.float32)
+    return GroupedLinearInputs(x=x, w=w, w_sf=sf, ws2=ws2)
 
 
 # ---------------------------------------------------------------------------
