@@ -45,6 +45,9 @@ WORKLOADS = {
     # router gate (FP8 round-tripped bf16 weight, top-8 softmax) at the decode and large-batch token counts
     "router_decode": dict(kind="router", T=64, H=7168, E=384, k=8),
     "router_4096": dict(kind="router", T=4096, H=7168, E=384, k=8),
+    # attention output projection wo_a: 8 groups of K 4096, output width 1024 per group
+    "wo_a_decode": dict(kind="grouped_linear", T=64, G=8, N=1024, K=4096),
+    "wo_a_4096": dict(kind="grouped_linear", T=4096, G=8, N=1024, K=4096),
     # dense NVFP4 linear at projection shapes
     "linear_q_a_m1": dict(kind="linear", M=1, N=1536, K=7168),
     "linear_q_a_m128": dict(kind="linear", M=128, N=1536, K=7168),
@@ -476,6 +479,81 @@ def run_router(args, cfg):
     }
 
 
+def run_grouped_linear(args, cfg):
+    """Grouped linear of the attention output projection (wo_a): x [T, G, K]
+    bf16 times G NVFP4 weights [N, K] (one nvfp4_grouped_linear call, the
+    fp16 staging of x included)."""
+    import numpy as np
+    import torch
+
+    from fp4_block_scaled_route_amd import ops, synth
+
+    t, g, n, k = cfg["T"], cfg["G"], cfg["N"], cfg["K"]
+    gi = synth.make_grouped_linear(t, g, n, k, seed=args.seed)
+    x = gi.x.cuda()
+    w_bytes = g * n * (k // 2 + k // 16)
+    copies = max(1, int(np.ceil(1.0e9 / (w_bytes + t * g * k * 2))))   # rotate past the last-level cache
+    ws = [(torch.from_numpy(gi.w).cuda(), torch.from_numpy(gi.w_sf).cuda()) for _ in range(min(copies, 64))]
+    ws2 = torch.from_numpy(gi.ws2).cuda()
+    xs = [x.clone() for _ in range(min(copies, 8))]
+    y = torch.empty((t, g, n), dtype=torch.bfloat16, device="cuda")
+    work = torch.empty(max(1, ops.grouped_linear_workspace_size(t, g, n, k)), dtype=torch.uint8, device="cuda")
+    nw, nx = len(ws), len(xs)
+    for i in range(args.warmup):
+        ops.grouped_linear(*ws[i % nw], ws2, x=xs[i % nx], out=y, workspace=work)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        ops.grouped_linear(*ws[i % nw], ws2, x=xs[i % nx], out=y, workspace=work)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = w_bytes + t * g * k * 2 + t * g * n * 2
+    flops = 2 * t * g * n * k
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfl = flops / (ms * 1e-3) / 1e12
+    bound_mfma = flops / nbytes > BF16_RIDGE_FLOP_PER_BYTE
+    if bound_mfma:
+        roof = dict(bound="mfma", achieved=round(tfl, 2), peak=FP16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tfl / FP16_PEAK_TFLOPS, 4), traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
+    roof.update(kernel="nvfp4_rows_to_f16 + grouped GEMM (one call)", kernel_ms=round(ms, 5),
+                algorithmic_bytes_per_launch=nbytes, algorithmic_flops_per_launch=flops)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import grouped_linear
+        log("timing the CPU oracle on a bounded sample ...")
+        xs64 = synth.bf16_to_float64(gi.x[:4])
+        t_start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t_start < 10.0:
+            grouped_linear.grouped_linear_bf16(xs64, gi.w, gi.w_sf, gi.ws2)
+            reps += 1
+        sec = (time.perf_counter() - t_start) / reps
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        sample_bytes = w_bytes + 4 * g * k * 2 + 4 * g * n * 2
+        cpu = dict(value=round(sample_bytes / sec / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                   sample=f"4 tokens against all {g} group weights, float64 numpy oracle, {reps} repetitions "
+                          f"in about 10 s")
+    return {
+        "metric": "wo_a grouped linear GB/s or TFLOP/s (%roofline), 1xMI355X",
+        "value": round(gbs if not bound_mfma else tfl, 3), "unit": "GB/s" if not bound_mfma else "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"grouped linear wo_a: {t} tokens x {g} groups, K {k} per group, width {n}, "
+                               f"NVFP4 weights, bf16 activations, {nw} rotating weight copies",
+                   "name": args.workload},
+        "tflops": round(tfl, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
 def run_copy(args):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE readings to bytes."""
@@ -516,7 +594,8 @@ def main():
         run_copy(args)
         return
     cfg = WORKLOADS[args.workload]
-    run = {"moe": run_moe, "linear": run_linear, "router": run_router}[cfg["kind"]]
+    run = {"moe": run_moe, "linear": run_linear, "router": run_router,
+           "grouped_linear": run_grouped_linear}[cfg["kind"]]
     res = run(args, cfg)
     print(json.dumps(res), flush=True)
 

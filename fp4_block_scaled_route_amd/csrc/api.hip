@@ -183,6 +183,82 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
   return launch_status(launch_gemm(g, amode, EPI_Y_BF16, sh, 1, s));
 }
 
+size_t nvfp4_grouped_linear_workspace_size(int64_t T, int64_t G, int64_t N, int64_t K) {
+  if (T <= 0 || G <= 0 || T * G >= kMaxDim) return 0;
+  return nvfp4_linear_workspace_size(T * G, N, K);
+}
+
+int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
+                         const uint8_t* w_fp4, const uint8_t* w_sf, const float* ws2, int64_t T, int64_t G, int64_t N,
+                         int64_t K, void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || G <= 0 || N <= 0 || K <= 0 || T >= kMaxDim || G >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return NVFP4_ERR_SHAPE;
+  if (K % 256 != 0 || N % 16 != 0 || T * G >= kMaxDim || G * N >= kMaxDim) return NVFP4_ERR_SHAPE;
+  // every tensor a kernel reads through a buffer resource must span < 4 GiB
+  if (N * (K / 2) >= kMaxBuffer || T * G * K * 2 >= kMaxBuffer) return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  const bool fp4 = x_fp4 != nullptr;
+  if (fp4 && (x_bf16 || !x_sf || !gsa)) return x_bf16 ? NVFP4_ERR_ARG : NVFP4_ERR_NULL;
+  if (!fp4 && !x_bf16) return NVFP4_ERR_NULL;
+  if (!fp4 && (x_sf || gsa)) return NVFP4_ERR_ARG;
+  if (!w_fp4 || !w_sf || !ws2 || !y_bf16) return NVFP4_ERR_NULL;
+  if (!aligned(w_fp4, 16) || !aligned(w_sf, 16) || !aligned(ws2, 4) || !aligned(y_bf16, 16)) return NVFP4_ERR_ALIGN;
+  if (fp4 && (!aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gsa, 4))) return NVFP4_ERR_ALIGN;
+  if (!fp4 && !aligned(x_bf16, 16)) return NVFP4_ERR_ALIGN;
+  const int64_t rows = T * G;   // activation rows of K: row t * G + g
+  if (!fp4) {
+    if (!workspace || workspace_bytes < nvfp4_grouped_linear_workspace_size(T, G, N, K)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* rowshift = static_cast<int*>(workspace);
+  f16* x16 = fp4 ? nullptr
+                 : reinterpret_cast<f16*>(static_cast<uint8_t*>(workspace) + round_up(sizeof(int32_t) * (size_t)rows, 256));
+  if (!fp4) {
+    hipError_t e = launch_rows_to_f16(static_cast<const uint16_t*>(x_bf16), (int)rows, (int)K, rowshift, x16, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  }
+  GemmArgs g{};
+  g.w = w_fp4;
+  g.w_sf = w_sf;
+  g.w_ws2 = ws2;
+  g.w_gstride = N * (K / 2);
+  g.sf_gstride = N * (K / 16);
+  g.n_routed = (int)G;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.list_part = 2;
+  g.a = fp4 ? static_cast<const void*>(x_fp4) : static_cast<const void*>(x16);
+  g.a_rows = (int)rows;
+  g.a_sf = x_sf;
+  g.rowshift = fp4 ? nullptr : rowshift;
+  g.gsa = fp4 ? gsa : nullptr;
+  g.y = static_cast<uint16_t*>(y_bf16);
+  // Each group's T rows: up to 4 rows on the barrier-free kernels; on the
+  // 8-wave kernel in 112-row passes when that gives at least one work item
+  // (group, pass, 512-row block) per CU (K a multiple of 1024); otherwise on
+  // the 4-wave kernel (more, smaller work items: at decode sizes the launch
+  // is a latency chain per item).  Every pass is a work item of its own.
+  GemmShape sh{1, 2};
+  int pr = (int)T;
+  if (T > kBigGroupRows) {
+    const int64_t items8 = G * ((T + 111) / 112) * ((N + 511) / 512);
+    if (items8 >= 256 && K % 1024 == 0) {
+      sh = GemmShape{7, 4, 8};
+    } else {
+      sh = GemmShape{pick_maxc((double)T), 2};
+    }
+    pr = 16 * sh.maxc;
+  }
+  g.gl_T = (int)T;
+  g.gl_G = (int)G;
+  g.gl_pr = pr;
+  g.gl_npass = (int)((T + pr - 1) / pr);
+  const int brows = gemm_rows_per_block(EPI_Y_BF16, sh);
+  g.nb = (int)((N + brows - 1) / brows);
+  return launch_status(launch_gemm(g, fp4 ? A_FP4 : A_F16, EPI_Y_BF16, sh, (int)G * g.gl_npass, s));
+}
+
 size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared,
                                 int h_fp4) {
   if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;

@@ -96,6 +96,12 @@ __device__ __forceinline__ bool resolve_item(const GemmArgs& a, int gi, Item& it
     it.g = a.glist[gi];
     it.row0 = a.offsets[it.g];
     it.m = a.offsets[it.g + 1] - it.row0;
+  } else if (a.gl_G) {
+    const int g = gi / a.gl_npass, p = gi - g * a.gl_npass;
+    if (g >= a.gl_G) return false;
+    it.g = g;
+    it.row0 = g * a.gl_T + p * a.gl_pr;
+    it.m = min(a.gl_pr, a.gl_T - p * a.gl_pr);
   } else {
     if (gi > 0) return false;
     it.g = 0;
@@ -113,6 +119,10 @@ __device__ __forceinline__ bool resolve_item(const GemmArgs& a, int gi, Item& it
 
 // Activation row (in the A tensor) of sorted row r.
 __device__ __forceinline__ int a_row_of(const GemmArgs& a, int r) {
+  if (a.gl_G) {
+    const int g = r / a.gl_T;
+    return (r - g * a.gl_T) * a.gl_G + g;
+  }
   if (!a.a_by_token || !a.offsets) return r;
   const int pid = a.perm[r];
   return pid < a.P ? pid / a.topk : pid - a.P;
@@ -256,7 +266,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
       const int tr = pbase + 16 * c + lr;
       if (c >= nc || tr >= mlim) continue;
       const int r = it.row0 + tr;
-      const int sh = shift_of(a, a_row_of(a, r));
+      const int arow = a_row_of(a, r);
+      const int sh = shift_of(a, arow);
 #pragma unroll
       for (int f = 0; f < R; ++f) {
         if (!fr.fvalid[f]) continue;
@@ -268,7 +279,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
         o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
         o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
         if constexpr (EP == EPI_Y_BF16) {
-          *reinterpret_cast<uint2*>(a.y + (int64_t)r * a.N + n0) = o;
+          // output row = activation row (dense: r; grouped linear: t * G + g)
+          *reinterpret_cast<uint2*>(a.y + (int64_t)arow * a.N + n0) = o;
         } else {
           const int pid = a.perm[r];
           *reinterpret_cast<uint2*>(a.slot + (int64_t)pid * a.N + n0) = o;

@@ -61,6 +61,11 @@ struct GemmArgs {
   const int* gcount;
   int list_part;
   int M;               // dense row count
+  // Grouped linear (gl_G > 0, offsets == nullptr): gl_G groups of gl_T rows;
+  // sorted row r = g * gl_T + t is activation and output row t * gl_G + g
+  // (the [T, G, K] -> [T, G, N] layout); work item = (group, pass of gl_pr rows),
+  // gl_npass passes per group.
+  int gl_T, gl_G, gl_npass, gl_pr;
   int nb;              // weight-row blocks per group (grid = groups * nb)
   // Activation operand.
   const void* a;       // see AMode; row pitch in elements = K

@@ -25,6 +25,8 @@ EXPORTED = (
     "nvfp4_quantize_act",
     "nvfp4_linear_workspace_size",
     "nvfp4_linear",
+    "nvfp4_grouped_linear_workspace_size",
+    "nvfp4_grouped_linear",
     "nvfp4_moe_workspace_size",
     "nvfp4_moe_grouped",
     "nvfp4_router_prepare",
@@ -80,6 +82,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear.restype = ctypes.c_int
         L.nvfp4_linear.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                    _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]
+        L.nvfp4_grouped_linear_workspace_size.restype = ctypes.c_size_t
+        L.nvfp4_grouped_linear_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64]
+        L.nvfp4_grouped_linear.restype = ctypes.c_int
+        L.nvfp4_grouped_linear.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                           _c_i64, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]
         L.nvfp4_moe_workspace_size.restype = ctypes.c_size_t
         L.nvfp4_moe_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
         L.nvfp4_moe_grouped.restype = ctypes.c_int
@@ -155,6 +162,31 @@ def linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Optional[t
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().nvfp4_linear(_p(x), _p(x_fp4), _p(x_sf), _p(gsa), _p(w), _p(w_sf), _p(ws2),
                               m, n, k, _p(y), _p(workspace), wsb, _stream()))
+    return y
+
+
+def grouped_linear_workspace_size(t: int, g: int, n: int, k: int) -> int:
+    return int(lib().nvfp4_grouped_linear_workspace_size(t, g, n, k))
+
+
+def grouped_linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Optional[torch.Tensor] = None,
+                   x_fp4: Optional[torch.Tensor] = None, x_sf: Optional[torch.Tensor] = None,
+                   gsa: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[T, G, N] with y[:, g] = x[:, g] @ W[g]^T (bf16 out).  Weights
+    ``w`` [G, N, K/2], ``w_sf`` [G, N, K/16], ``ws2`` [G].  Activations: ``x``
+    bf16 [T, G, K], or ``x_fp4`` [T, G, K/2] + ``x_sf`` [T, G, K/16] + ``gsa`` [1]."""
+    g, n, kh = w.shape
+    k = kh * 2
+    t = (x if x is not None else x_fp4).shape[0]
+    dev = w.device
+    y = out if out is not None else torch.empty((t, g, n), dtype=torch.bfloat16, device=dev)
+    need = lib().nvfp4_grouped_linear_workspace_size(t, g, n, k)
+    if workspace is None and need and x is not None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().nvfp4_grouped_linear(_p(x), _p(x_fp4), _p(x_sf), _p(gsa), _p(w), _p(w_sf), _p(ws2),
+                                      t, g, n, k, _p(y), _p(workspace), wsb, _stream()))
     return y
 
 

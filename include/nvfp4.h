@@ -110,6 +110,31 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_grouped_linear - NVFP4 grouped linear of the attention output
+ * projection wo_a: G groups, y[t, g, :] = x[t, g, :] @ W[g]^T, bf16 out, fp32
+ * accumulation (page "commit 4c6464e - vllm": the notes on the BF16 wo_a
+ * path, a batched matmul over n_local_groups groups of in_features 4096, and
+ * on replacing it with an NVFP4 grouped linear over those groups).
+ *   Activations [T, G, K] (token-major, as the [T, G*K] attention output is
+ *   laid out), one of:
+ *     x_bf16 [T, G, K] bf16 (then x_fp4, x_sf, gsa must be NULL), or
+ *     x_fp4 [T, G, K/2] + x_sf [T, G, K/16] + gsa (device fp32 scalar), from
+ *     nvfp4_quantize_act on the [T * G, K] view (one global scale).
+ *   w_fp4 [G, N, K/2], w_sf [G, N, K/16]; ws2 [G] device fp32, each group's
+ *   weight_scale_2.
+ *   y_bf16 [T, G, N] bf16 output, fully overwritten.
+ *   workspace: device scratch of nvfp4_grouped_linear_workspace_size(T, G, N, K)
+ *   bytes for bf16 activations (NULL allowed with NVFP4 activations).
+ *   Requires K % 256 == 0, N % 16 == 0, 16-byte aligned tensors.
+ * Errors: as nvfp4_linear.
+ */
+size_t nvfp4_grouped_linear_workspace_size(int64_t T, int64_t G, int64_t N, int64_t K);
+int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
+                         const uint8_t* w_fp4, const uint8_t* w_sf, const float* ws2,
+                         int64_t T, int64_t G, int64_t N, int64_t K, void* y_bf16,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_moe_grouped - one Mixture-of-Experts layer with NVFP4 experts.
  * Routed experts (stacked (E, N, K), page "commit efe63ca", note on stacking
  * experts; one weight_scale_2 per expert and layer, same page, note on

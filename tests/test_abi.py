@@ -64,6 +64,31 @@ def test_linear_validation(lib):
     assert call(args(wb=4)) == -4
 
 
+def test_grouped_linear_validation(lib):
+    L = lib
+    ws = L.nvfp4_grouped_linear_workspace_size(64, 8, 1024, 4096)
+    assert ws >= 64 * 8 * 4096 * 2
+    args = lambda **kw: dict(dict(x=FAKE, xq=None, xs=None, gsa=None, w=FAKE, ws=FAKE, ws2=FAKE,  # noqa: E731
+                                  T=64, G=8, N=1024, K=4096, y=FAKE, work=FAKE, wb=ws), **kw)
+
+    def call(a):
+        return L.nvfp4_grouped_linear(a["x"], a["xq"], a["xs"], a["gsa"], a["w"], a["ws"], a["ws2"],
+                                      a["T"], a["G"], a["N"], a["K"], a["y"], a["work"], a["wb"], None)
+    assert call(args(K=4000)) == -2         # K not a multiple of 256
+    assert call(args(N=1000)) == -2         # N not a multiple of 16
+    assert call(args(G=0)) == -2
+    assert call(args(T=-1)) == -2
+    assert call(args(T=0)) == 0             # nothing to do, nothing launched
+    assert call(args(ws2=None)) == -1
+    assert call(args(x=None)) == -1
+    assert call(args(xq=FAKE)) == -6        # both activation forms
+    assert call(args(x=None, xq=FAKE, xs=FAKE)) == -1       # NVFP4 activations without their global scale
+    assert call(args(y=ctypes.c_void_p(0x1004))) == -3
+    assert call(args(ws2=ctypes.c_void_p(0x1002))) == -3
+    assert call(args(work=None)) == -4
+    assert call(args(wb=ws - 1)) == -4
+
+
 def test_quantize_validation(lib):
     L = lib
     assert L.nvfp4_quantize_act(FAKE, 4, 40, FAKE, 1, FAKE, FAKE, None) == -2
