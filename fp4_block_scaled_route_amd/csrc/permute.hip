@@ -81,6 +81,7 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
 
   __shared__ int hist[kPermWaves][kMaxExperts];
   __shared__ int goff[kMaxExperts + 2];
+  __shared__ __attribute__((aligned(16))) int gsize[kMaxExperts + 4];   // rows of each group (phase 4)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.T * a.topk;
@@ -90,10 +91,19 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
   for (int i = tid; i < kPermWaves * E; i += blockDim.x) hist[i / E][i % E] = 0;
   __syncthreads();
 
-  // 1. per-wave histograms
-  for (int f = f0 + lane; f < f1; f += 64) {
-    const int id = a.ids[f];
-    if (id >= 0 && id < E) atomicAdd(&hist[wave][id], 1);
+  // 1. per-wave histograms (ids read kBatch iterations at a time, so the
+  // global load latency is paid once per batch)
+  constexpr int kBatch = 8;
+  for (int fb = f0; fb < f1; fb += 64 * kBatch) {
+    int idv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int f = fb + 64 * u + lane;
+      idv[u] = f < f1 ? a.ids[f] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (idv[u] >= 0 && idv[u] < E) atomicAdd(&hist[wave][idv[u]], 1);
   }
   __syncthreads();
 
@@ -135,12 +145,24 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
   }
   __syncthreads();
 
-  // 3. stable ranks
+  // 3. stable ranks (ids again read kBatch iterations at a time)
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
+  int idv[kBatch];
   for (int base = f0; base < f1; base += 64) {
+    const int u = ((base - f0) >> 6) % kBatch;   // wave-uniform
+    if (u == 0) {
+#pragma unroll
+      for (int v = 0; v < kBatch; ++v) {
+        const int fv = base + 64 * v + lane;
+        idv[v] = fv < f1 ? a.ids[fv] : -1;
+      }
+    }
     const int f = base + lane;
-    int id = f < f1 ? a.ids[f] : -1;
+    int id = -1;
+#pragma unroll
+    for (int v = 0; v < kBatch; ++v)
+      if (v == u) id = idv[v];
     if (id < 0 || id >= E) id = -1;
     uint64_t peers = __ballot(id >= 0);
 #pragma unroll 1
@@ -177,15 +199,24 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
     if (a.offsets_out) a.offsets_out[i] = goff[i];
   }
 
-  // 4. group order: non-empty groups, largest first, ties by id
+  // 4. group order: non-empty groups, largest first, ties by id.  Group g's
+  // rank counts the groups before it; the sizes are read four at a time (one
+  // 16-byte LDS read, the same address in every lane).
   const int G = E + (a.shared ? 1 : 0);
+  const int G4 = (G + 3) & ~3;
+  for (int h = tid; h < G4; h += blockDim.x) gsize[h] = h < G ? goff[h + 1] - goff[h] : -1;
+  __syncthreads();
   for (int g = tid; g < G; g += blockDim.x) {
-    const int mg = goff[g + 1] - goff[g];
+    const int mg = gsize[g];
     if (mg <= 0) continue;
     int rank = 0;
-    for (int h = 0; h < G; ++h) {
-      const int mh = goff[h + 1] - goff[h];
-      rank += (mh > mg) || (mh == mg && h < g);
+#pragma unroll 4
+    for (int h = 0; h < G4; h += 4) {
+      const int4 m4 = *reinterpret_cast<const int4*>(&gsize[h]);
+      rank += (m4.x > mg) || (m4.x == mg && h < g);
+      rank += (m4.y > mg) || (m4.y == mg && h + 1 < g);
+      rank += (m4.z > mg) || (m4.z == mg && h + 2 < g);
+      rank += (m4.w > mg) || (m4.w == mg && h + 3 < g);
     }
     a.glist[rank] = g;
   }
