@@ -206,8 +206,15 @@ struct Frags {
     const int k1 = min(8 * sc + 4 + lg, nkc - 1);
 #pragma unroll
     for (int f = 0; f < R; ++f) {
-      raw[f][0] = buf_load16(rs, vs - lg * 4 + k0 * 16, ss[f]);
-      raw[f][1] = buf_load16(rs, vs - lg * 4 + k1 * 16, ss[f]);
+      // (down GEMM: with the non-temporal hint, measured 3% faster on MI355X;
+      // gate/up: 8% slower with it)
+      if constexpr (EP == EPI_SLOT) {
+        raw[f][0] = buf_load16_nt(rs, vs - lg * 4 + k0 * 16, ss[f]);
+        raw[f][1] = buf_load16_nt(rs, vs - lg * 4 + k1 * 16, ss[f]);
+      } else {
+        raw[f][0] = buf_load16(rs, vs - lg * 4 + k0 * 16, ss[f]);
+        raw[f][1] = buf_load16(rs, vs - lg * 4 + k1 * 16, ss[f]);
+      }
     }
   }
 
