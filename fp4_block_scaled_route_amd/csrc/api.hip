@@ -183,9 +183,55 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
   return launch_status(launch_gemm(g, amode, EPI_Y_BF16, sh, 1, s));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Launch plan of the grouped linear: kernel shape, rows per pass, K splits.
+// Each group's T rows: up to 4 rows on the barrier-free kernels; on the
+// 8-wave kernel in 112-row passes when that gives at least one work item
+// (group, pass, 512-row block) per CU (K a multiple of 1024); otherwise on
+// the 4-wave kernel, whose work items are latency chains over K: when they
+// are too few to fill the GPU, K is split (2, 4 or 8 parts of at least
+// two 256-element chunks) and the fp32 partial sums are added in split order.
+struct GlPlan {
+  GemmShape sh{1, 2};
+  int pr = 0, npass = 1, ksplit = 1, nb = 1;
+};
+
+GlPlan gl_plan(int64_t T, int64_t G, int64_t N, int64_t K) {
+  GlPlan p;
+  p.pr = (int)T;
+  if (T > kBigGroupRows) {
+    const int64_t items8 = G * ((T + 111) / 112) * ((N + 511) / 512);
+    if (items8 >= 256 && K % 1024 == 0) {
+      p.sh = GemmShape{7, 4, 8};
+    } else {
+      p.sh = GemmShape{pick_maxc((double)T), 2};
+    }
+    p.pr = 16 * p.sh.maxc;
+  }
+  p.npass = (int)((T + p.pr - 1) / p.pr);
+  const int brows = gemm_rows_per_block(EPI_Y_BF16, p.sh);
+  p.nb = (int)((N + brows - 1) / brows);
+  if (p.sh.maxc > 1 && p.sh.nw == 4) {
+    const int64_t items = G * p.npass * p.nb;
+    const int64_t nkc = K / 256;
+    while (p.ksplit < 8 && items * p.ksplit * 2 <= 256 && nkc % (p.ksplit * 2) == 0 && nkc / (p.ksplit * 2) >= 2)
+      p.ksplit *= 2;
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t nvfp4_grouped_linear_workspace_size(int64_t T, int64_t G, int64_t N, int64_t K) {
-  if (T <= 0 || G <= 0 || T * G >= kMaxDim) return 0;
-  return nvfp4_linear_workspace_size(T * G, N, K);
+  if (T <= 0 || G <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || T * G >= kMaxDim) return 0;
+  const GlPlan p = gl_plan(T, G, N, K);
+  const size_t part = p.ksplit > 1 ? round_up(sizeof(float) * (size_t)p.ksplit * T * G * N, 256) : 0;
+  return nvfp4_linear_workspace_size(T * G, N, K) + part;
 }
 
 int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
@@ -206,14 +252,16 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
   if (fp4 && (!aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gsa, 4))) return NVFP4_ERR_ALIGN;
   if (!fp4 && !aligned(x_bf16, 16)) return NVFP4_ERR_ALIGN;
   const int64_t rows = T * G;   // activation rows of K: row t * G + g
-  if (!fp4) {
+  const GlPlan plan = gl_plan(T, G, N, K);
+  if (!fp4 || plan.ksplit > 1) {
     if (!workspace || workspace_bytes < nvfp4_grouped_linear_workspace_size(T, G, N, K)) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int* rowshift = static_cast<int*>(workspace);
-  f16* x16 = fp4 ? nullptr
-                 : reinterpret_cast<f16*>(static_cast<uint8_t*>(workspace) + round_up(sizeof(int32_t) * (size_t)rows, 256));
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  int* rowshift = reinterpret_cast<int*>(wsp);
+  f16* x16 = fp4 ? nullptr : reinterpret_cast<f16*>(wsp + round_up(sizeof(int32_t) * (size_t)rows, 256));
+  float* part = plan.ksplit > 1 ? reinterpret_cast<float*>(wsp + nvfp4_linear_workspace_size(rows, N, K)) : nullptr;
   if (!fp4) {
     hipError_t e = launch_rows_to_f16(static_cast<const uint16_t*>(x_bf16), (int)rows, (int)K, rowshift, x16, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
@@ -234,29 +282,17 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
   g.rowshift = fp4 ? nullptr : rowshift;
   g.gsa = fp4 ? gsa : nullptr;
   g.y = static_cast<uint16_t*>(y_bf16);
-  // Each group's T rows: up to 4 rows on the barrier-free kernels; on the
-  // 8-wave kernel in 112-row passes when that gives at least one work item
-  // (group, pass, 512-row block) per CU (K a multiple of 1024); otherwise on
-  // the 4-wave kernel (more, smaller work items: at decode sizes the launch
-  // is a latency chain per item).  Every pass is a work item of its own.
-  GemmShape sh{1, 2};
-  int pr = (int)T;
-  if (T > kBigGroupRows) {
-    const int64_t items8 = G * ((T + 111) / 112) * ((N + 511) / 512);
-    if (items8 >= 256 && K % 1024 == 0) {
-      sh = GemmShape{7, 4, 8};
-    } else {
-      sh = GemmShape{pick_maxc((double)T), 2};
-    }
-    pr = 16 * sh.maxc;
-  }
   g.gl_T = (int)T;
   g.gl_G = (int)G;
-  g.gl_pr = pr;
-  g.gl_npass = (int)((T + pr - 1) / pr);
-  const int brows = gemm_rows_per_block(EPI_Y_BF16, sh);
-  g.nb = (int)((N + brows - 1) / brows);
-  return launch_status(launch_gemm(g, fp4 ? A_FP4 : A_F16, EPI_Y_BF16, sh, (int)G * g.gl_npass, s));
+  g.gl_pr = plan.pr;
+  g.gl_npass = plan.npass;
+  g.nb = plan.nb;
+  const int items = (int)G * plan.npass * plan.ksplit;
+  if (plan.ksplit == 1) return launch_status(launch_gemm(g, fp4 ? A_FP4 : A_F16, EPI_Y_BF16, plan.sh, items, s));
+  g.ksplit = plan.ksplit;
+  g.part = part;
+  if (launch_gemm(g, fp4 ? A_FP4 : A_F16, EPI_PART_F32, plan.sh, items, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  return launch_status(launch_split_reduce(part, plan.ksplit, rows * N, static_cast<uint16_t*>(y_bf16), s));
 }
 
 size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared,

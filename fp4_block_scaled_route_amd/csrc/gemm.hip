@@ -82,12 +82,14 @@ constexpr int kVmcnt0 = 0x0F70;
 // Resolved work item.
 struct Item {
   int g, row0, m;
+  int ks;              // K split (grouped linear), else 0
   const uint8_t* W;
   const uint8_t* WS;
   float alpha;
 };
 
 __device__ __forceinline__ bool resolve_item(const GemmArgs& a, int gi, Item& it) {
+  it.ks = 0;
   if (a.offsets) {
     const int lo = a.list_part == 1 ? a.gcount[1] : 0;
     const int hi = a.list_part == 0 ? a.gcount[1] : a.gcount[0];
@@ -97,6 +99,11 @@ __device__ __forceinline__ bool resolve_item(const GemmArgs& a, int gi, Item& it
     it.row0 = a.offsets[it.g];
     it.m = a.offsets[it.g + 1] - it.row0;
   } else if (a.gl_G) {
+    if (a.ksplit > 1) {
+      const int gi2 = gi / a.ksplit;
+      it.ks = gi - gi2 * a.ksplit;
+      gi = gi2;
+    }
     const int g = gi / a.gl_npass, p = gi - g * a.gl_npass;
     if (g >= a.gl_G) return false;
     it.g = g;
@@ -267,7 +274,26 @@ __device__ __forceinline__ void transpose4(u32x4& v) {
 template <int R, int MAXC, int EP, int NW>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, const Frags<R, EP, NW>& fr,
                                          f32x4 (&acc)[R][MAXC], int nc, int pbase, int mlim, int lr, int lg) {
-  if constexpr (EP == EPI_Y_BF16 || EP == EPI_SLOT) {
+  if constexpr (EP == EPI_PART_F32) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int tr = pbase + 16 * c + lr;
+      if (c >= nc || tr >= mlim) continue;
+      const int arow = a_row_of(a, it.row0 + tr);
+      const int sh = shift_of(a, arow);
+#pragma unroll
+      for (int f = 0; f < R; ++f) {
+        if (!fr.fvalid[f]) continue;
+        const int n0 = fr.fbase[f] + 4 * lg;
+        float4 v;
+        v.x = __builtin_ldexpf(acc[f][c][0], -sh) * it.alpha;
+        v.y = __builtin_ldexpf(acc[f][c][1], -sh) * it.alpha;
+        v.z = __builtin_ldexpf(acc[f][c][2], -sh) * it.alpha;
+        v.w = __builtin_ldexpf(acc[f][c][3], -sh) * it.alpha;
+        *reinterpret_cast<float4*>(a.part + ((int64_t)it.ks * a.a_rows + arow) * a.N + n0) = v;
+      }
+    }
+  } else if constexpr (EP == EPI_Y_BF16 || EP == EPI_SLOT) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int tr = pbase + 16 * c + lr;
@@ -658,7 +684,9 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   Frags<R, EP, NW> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
-  const int nkc = K / kChunk;
+  // chunks of this item: [kbase, kbase + nkc) (all of K unless K is split)
+  const int nkc = K / kChunk / (a.ksplit > 1 ? a.ksplit : 1);
+  const int kbase = it.ks * nkc;
   const int last = nkc - 1;
   const int seg = AM == A_F16 ? lane & 31 : lg;
   const int rsub = AM == A_F16 ? 2 * wave + (lane >> 5) : 16 * wave + lr;
@@ -695,6 +723,7 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     const int nsw = __builtin_amdgcn_readfirstlane((prow + RSTEP - 1) / RSTEP);
 
     auto stage_load = [&](int kc) {
+      kc += kbase;
 #pragma unroll
       for (int i = 0; i < SROWS; ++i) {
         if (DB && i >= nsw) break;
@@ -831,7 +860,7 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       fr.load_codes(wb.c0, wb.c1, 0);
       load_quad(0);
     } else {
-      fr.load(wb, 0);
+      fr.load(wb, kbase);
     }
     stage_load(0);
     stage_write(0);
@@ -870,13 +899,13 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       for (; kc + 1 < nkc; kc += 2) {
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
         stage_load(kc + 1);
-        fr.load(wb1, kc + 1);
+        fr.load(wb1, kbase + kc + 1);
         compute(0, wb, kc + 1, 0);
         stage_write(1);
         __syncthreads();
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
         stage_load(min(kc + 2, last));
-        fr.load(wb, min(kc + 2, last));
+        fr.load(wb, kbase + min(kc + 2, last));
         compute(1, wb1, min(kc + 2, last), 0);
         stage_write(0);
         __syncthreads();
@@ -940,7 +969,32 @@ hipError_t dispatch(const GemmArgs& a, GemmShape sh, int n_groups, hipStream_t s
   }
 }
 
+__global__ __launch_bounds__(256) void nvfp4_split_reduce(const float4* part, int S, int64_t n4, uint2* y) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  float4 v = part[i];
+  for (int s = 1; s < S; ++s) {
+    const float4 u = part[(int64_t)s * n4 + i];
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  uint2 o;
+  o.x = float_to_bf16_bits(v.x) | (float_to_bf16_bits(v.y) << 16);
+  o.y = float_to_bf16_bits(v.z) | (float_to_bf16_bits(v.w) << 16);
+  y[i] = o;
+}
+
 }  // namespace
+
+hipError_t launch_split_reduce(const float* part, int S, int64_t n, uint16_t* y, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(nvfp4_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(part), S, n4, reinterpret_cast<uint2*>(y));
+  return hipGetLastError();
+}
 
 int gemm_rows_per_block(int epi, GemmShape sh) {
   const bool sw = epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4;
@@ -956,6 +1010,12 @@ hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, GemmShape sh, int 
   if (amode == A_FP4 && epi == EPI_SWIGLU_FP4) return dispatch<A_FP4, EPI_SWIGLU_FP4>(a, sh, n_groups, s);
   if (amode == A_F16 && epi == EPI_SLOT) return dispatch<A_F16, EPI_SLOT>(a, sh, n_groups, s);
   if (amode == A_FP4 && epi == EPI_SLOT) return dispatch<A_FP4, EPI_SLOT>(a, sh, n_groups, s);
+  if (epi == EPI_PART_F32) {
+    // K splits run on the four-wave LDS kernel only
+    if (sh.maxc == 1 || sh.nw != kNW || a.ksplit < 1) return hipErrorInvalidValue;
+    if (amode == A_F16) return dispatch<A_F16, EPI_PART_F32>(a, sh, n_groups, s);
+    if (amode == A_FP4) return dispatch<A_FP4, EPI_PART_F32>(a, sh, n_groups, s);
+  }
   return hipErrorInvalidValue;
 }
 

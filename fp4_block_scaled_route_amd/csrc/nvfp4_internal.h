@@ -34,7 +34,8 @@ enum EpiMode {
   EPI_Y_BF16 = 0,      // y[row, n] = bf16(alpha * acc)                    (dense linear)
   EPI_SWIGLU_F32 = 1,  // h[row, i] = silu(alpha*gate) * (alpha*up), fp32, + row max |h|
   EPI_SWIGLU_FP4 = 2,  // same h, quantized to NVFP4 with a supplied global scale
-  EPI_SLOT = 3         // slot[pair, n] = bf16(alpha * acc)                (down GEMM)
+  EPI_SLOT = 3,        // slot[pair, n] = bf16(alpha * acc)                (down GEMM)
+  EPI_PART_F32 = 4     // part[ks, row, n] = alpha * acc, fp32 (one K split of the grouped linear)
 };
 
 struct GemmArgs {
@@ -66,6 +67,11 @@ struct GemmArgs {
   // (the [T, G, K] -> [T, G, N] layout); work item = (group, pass of gl_pr rows),
   // gl_npass passes per group.
   int gl_T, gl_G, gl_npass, gl_pr;
+  // K split of the grouped linear (four-wave LDS kernel only): ksplit parts
+  // of K / ksplit each, item = ((group, pass), split); partial sums to part
+  // (EPI_PART_F32), added in split order by launch_split_reduce.
+  int ksplit;
+  float* part;
   int nb;              // weight-row blocks per group (grid = groups * nb)
   // Activation operand.
   const void* a;       // see AMode; row pitch in elements = K
@@ -137,6 +143,9 @@ struct CombineArgs {
   uint16_t* y;          // [T, H] bf16
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// y[i] = bf16(sum over s = 0..S-1, in that order, of part[s * n + i]), n % 4 == 0.
+hipError_t launch_split_reduce(const float* part, int S, int64_t n, uint16_t* y, hipStream_t stream);
 
 // word = max |x| over n bf16 values (n % 8 == 0), as a float (zeroed first).
 hipError_t launch_bf16_amax(const uint16_t* x, int64_t n, float* word, hipStream_t stream);

@@ -182,7 +182,7 @@ def grouped_linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Op
     dev = w.device
     y = out if out is not None else torch.empty((t, g, n), dtype=torch.bfloat16, device=dev)
     need = lib().nvfp4_grouped_linear_workspace_size(t, g, n, k)
-    if workspace is None and need and x is not None:
+    if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().nvfp4_grouped_linear(_p(x), _p(x_fp4), _p(x_sf), _p(gsa), _p(w), _p(w_sf), _p(ws2),

@@ -124,7 +124,10 @@ int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, 
  *   weight_scale_2.
  *   y_bf16 [T, G, N] bf16 output, fully overwritten.
  *   workspace: device scratch of nvfp4_grouped_linear_workspace_size(T, G, N, K)
- *   bytes for bf16 activations (NULL allowed with NVFP4 activations).
+ *   bytes, 256-byte aligned (the fp16 copy of bf16 activations, and fp32
+ *   partial sums when the call splits K: with few tokens the work is split
+ *   along K and the partial sums are added in a fixed order); contents
+ *   undefined after the call, not shared with a concurrent call.
  *   Requires K % 256 == 0, N % 16 == 0, 16-byte aligned tensors.
  * Errors: as nvfp4_linear.
  */
