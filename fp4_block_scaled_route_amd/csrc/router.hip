@@ -56,7 +56,7 @@ __global__ void nvfp4_router_scale_finish(float* scale) { scale[0] = scale[0] / 
 // 32-wide K step, three steps in flight.  Lane (r, g) loads 16 bytes (8 bf16)
 // at K offset 8g of each step for its row r; rows past T or E re-read the last
 // row (in bounds, results not written).  Partial tiles go to part[ks][t][e];
-// the selection adds the splits in order.
+// the selection adds the splits in a fixed order.
 constexpr int kRT = 64;    // tokens per workgroup
 constexpr int kRE = 128;   // experts per workgroup
 
@@ -133,41 +133,58 @@ __global__ __launch_bounds__(256) void nvfp4_router_logits(const uint16_t* x, co
   }
 }
 
-// Top-k softmax: one wave per token; lane l holds logits l, l + 64, ...,
-// each the sum of the K-split partials in split order (also written out).
+// Top-k softmax: one workgroup of 4 waves per token.  Wave w adds the
+// K-split partials s = w, w + 4, w + 8, ... in increasing s (4 splits per
+// batch of loads); wave 0 then adds the four wave sums in wave order (a fixed
+// order, so the logits do not depend on timing), writes them, and selects:
+// lane l holds logits l, l + 64, ...
 constexpr int kMaxPerLane = 8;   // E <= 512
+constexpr int kSelWaves = 4;
 
 __global__ __launch_bounds__(256) void nvfp4_router_select(const float* part, int ksplit, int T, int E, int topk,
                                                            float* logits, int32_t* ids, float* wts) {
+  __shared__ float wsum[kSelWaves][kMaxPerLane * 64];
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
   const int64_t sstride = (int64_t)T * E;
+  bool valid[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) valid[j] = lane + 64 * j < E;
   float v[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) v[j] = 0.0f;
+  const float* p = part + (int64_t)t * E + lane;
+  for (int s0 = wave; s0 < ksplit; s0 += 4 * kSelWaves) {
+    float q[4][kMaxPerLane];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = s0 + kSelWaves * u;
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j) q[u][j] = (sp < ksplit && valid[j]) ? p[(int64_t)sp * sstride + 64 * j] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j)
+        if (s0 + kSelWaves * u < ksplit) v[j] = (s0 + kSelWaves * u == wave) ? q[u][j] : v[j] + q[u][j];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) wsum[wave][lane + 64 * j] = v[j];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    float a = wsum[0][lane + 64 * j];
+    for (int w = 1; w < kSelWaves && w < ksplit; ++w) a += wsum[w][lane + 64 * j];
+    v[j] = a;
+  }
   bool taken[kMaxPerLane];
 #pragma unroll
   for (int j = 0; j < kMaxPerLane; ++j) {
-    v[j] = 0.0f;
-    taken[j] = lane + 64 * j >= E;
+    taken[j] = !valid[j];
+    if (valid[j]) logits[(int64_t)t * E + lane + 64 * j] = v[j];
   }
-  // partial sums added in split order; loads issued four splits at a time
-  const float* p = part + (int64_t)t * E + lane;
-  for (int k0 = 0; k0 < ksplit; k0 += 4) {
-    float q[4][kMaxPerLane];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j)
-        q[u][j] = (k0 + u < ksplit && !taken[j]) ? p[(int64_t)(k0 + u) * sstride + 64 * j] : 0.0f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j)
-        if (k0 + u < ksplit) v[j] = (k0 + u == 0) ? q[u][j] : v[j] + q[u][j];
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j)
-    if (!taken[j]) logits[(int64_t)t * E + lane + 64 * j] = v[j];
   float top = 0.0f, zsum = 0.0f;
   float sel_v = 0.0f;   // lane s keeps the s-th selected value
   int sel_i = 0;
@@ -237,7 +254,8 @@ hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_rt, int T, in
   const int ks = router_ksplit(T, H, E);
   hipLaunchKernelGGL(nvfp4_router_logits, dim3((T + kRT - 1) / kRT, (E + kRE - 1) / kRE, ks), dim3(256), 0, s, x,
                      w_rt, T, H, E, ks, part);
-  hipLaunchKernelGGL(nvfp4_router_select, dim3((T + 3) / 4), dim3(256), 0, s, part, ks, T, E, topk, logits, ids, wts);
+  hipLaunchKernelGGL(nvfp4_router_select, dim3(T), dim3(64 * kSelWaves), 0, s, part, ks, T, E, topk, logits, ids,
+                     wts);
   return hipGetLastError();
 }
 
