@@ -50,7 +50,10 @@ WORKLOADS = {
     "wo_a_4096": dict(kind="grouped_linear", T=4096, G=8, N=1024, K=4096),
     # dense NVFP4 linear at projection shapes
     "linear_q_a_m1": dict(kind="linear", M=1, N=1536, K=7168),
+    "linear_q_a_m32": dict(kind="linear", M=32, N=1536, K=7168),
     "linear_q_a_m128": dict(kind="linear", M=128, N=1536, K=7168),
+    "linear_q_b_m1": dict(kind="linear", M=1, N=24576, K=1536),
+    "linear_q_b_m32": dict(kind="linear", M=32, N=24576, K=1536),
     "linear_q_b_m128": dict(kind="linear", M=128, N=24576, K=1536),
 }
 

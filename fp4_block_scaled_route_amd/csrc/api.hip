@@ -126,80 +126,26 @@ int nvfp4_router_topk(const void* x_bf16, const void* w_rt_bf16, int64_t T, int6
                                           static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
-size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
-  (void)N;
-  if (M <= 0 || K <= 0) return 0;
-  return round_up(sizeof(int32_t) * (size_t)M, 256) + round_up(sizeof(uint16_t) * (size_t)M * K, 256);
-}
-
-int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
-                 const uint8_t* w_fp4, const uint8_t* w_sf, const float* gsb, int64_t M, int64_t N, int64_t K,
-                 void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
-  if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return NVFP4_ERR_SHAPE;
-  if (K % 256 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
-  // every tensor a kernel reads through a buffer resource must span < 4 GiB
-  if (N * (K / 2) >= kMaxBuffer || M * K * 2 >= kMaxBuffer) return NVFP4_ERR_SHAPE;
-  if (M == 0) return NVFP4_OK;
-  const bool fp4 = x_fp4 != nullptr;
-  if (fp4 && (x_bf16 || !x_sf || !gsa)) return x_bf16 ? NVFP4_ERR_ARG : NVFP4_ERR_NULL;
-  if (!fp4 && (!x_bf16)) return NVFP4_ERR_NULL;
-  if (!fp4 && (x_sf || gsa)) return NVFP4_ERR_ARG;
-  if (!w_fp4 || !w_sf || !gsb || !y_bf16) return NVFP4_ERR_NULL;
-  if (!aligned(w_fp4, 16) || !aligned(w_sf, 16) || !aligned(gsb, 4) || !aligned(y_bf16, 16)) return NVFP4_ERR_ALIGN;
-  if (fp4 && (!aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gsa, 4))) return NVFP4_ERR_ALIGN;
-  if (!fp4 && !aligned(x_bf16, 16)) return NVFP4_ERR_ALIGN;
-  const size_t need = nvfp4_linear_workspace_size(M, N, K);
-  if (!fp4 && need > 0) {
-    if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int* rowshift = static_cast<int*>(workspace);
-  f16* x16 = reinterpret_cast<f16*>(static_cast<uint8_t*>(workspace) + round_up(sizeof(int32_t) * (size_t)M, 256));
-  if (!fp4) {
-    hipError_t e = launch_rows_to_f16(static_cast<const uint16_t*>(x_bf16), (int)M, (int)K, rowshift, x16, s);
-    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-  }
-  GemmArgs g{};
-  g.w = w_fp4;
-  g.w_sf = w_sf;
-  g.w_ws2 = gsb;
-  g.n_routed = 1;
-  g.N = (int)N;
-  g.K = (int)K;
-  g.M = (int)M;
-  g.list_part = 2;
-  g.a = fp4 ? static_cast<const void*>(x_fp4) : static_cast<const void*>(x16);
-  g.a_rows = (int)M;
-  g.a_sf = x_sf;
-  g.rowshift = fp4 ? nullptr : rowshift;
-  g.gsa = fp4 ? gsa : nullptr;
-  g.y = static_cast<uint16_t*>(y_bf16);
-  const int amode = fp4 ? A_FP4 : A_F16;
-  const int maxc = M <= kBigGroupRows ? 1 : pick_maxc((double)M);
-  GemmShape sh{maxc, 2};
-  const int rows = gemm_rows_per_block(EPI_Y_BF16, sh);
-  g.nb = (int)((N + rows - 1) / rows);
-  return launch_status(launch_gemm(g, amode, EPI_Y_BF16, sh, 1, s));
-}
-
 }  // extern "C"
 
 namespace {
 
-// Launch plan of the grouped linear: kernel shape, rows per pass, K splits.
-// Each group's T rows: up to 4 rows on the barrier-free kernels; on the
-// 8-wave kernel in 112-row passes when that gives at least one work item
-// (group, pass, 512-row block) per CU (K a multiple of 1024); otherwise on
-// the 4-wave kernel, whose work items are latency chains over K: when they
-// are too few to fill the GPU, K is split (2, 4 or 8 parts of at least
-// two 256-element chunks) and the fp32 partial sums are added in split order.
+// Launch plan of the dense and grouped linear (G groups of T rows each; the
+// dense linear is G = 1).  Each group's T rows: up to 4 rows on the
+// barrier-free kernels; on the 8-wave kernel in 112-row passes when that
+// gives at least one work item (group, pass, 512-row block) per CU (K a
+// multiple of 1024); otherwise on the 4-wave kernel.  Work items on the
+// 4-wave and compact kernels are latency chains over K: when they are too
+// few to fill the GPU, K is split into S parts (S divides the 256-element
+// chunk count, at least 2 chunks per part, S <= 16) and the fp32 partial sums
+// are added in split order.  (NVFP4 activations on the barrier-free path are
+// not split.)
 struct GlPlan {
   GemmShape sh{1, 2};
   int pr = 0, npass = 1, ksplit = 1, nb = 1;
 };
 
-GlPlan gl_plan(int64_t T, int64_t G, int64_t N, int64_t K) {
+GlPlan gl_plan(int64_t T, int64_t G, int64_t N, int64_t K, bool fp4) {
   GlPlan p;
   p.pr = (int)T;
   if (T > kBigGroupRows) {
@@ -214,29 +160,39 @@ GlPlan gl_plan(int64_t T, int64_t G, int64_t N, int64_t K) {
   p.npass = (int)((T + p.pr - 1) / p.pr);
   const int brows = gemm_rows_per_block(EPI_Y_BF16, p.sh);
   p.nb = (int)((N + brows - 1) / brows);
-  if (p.sh.maxc > 1 && p.sh.nw == 4) {
+  if (p.sh.nw == 4 && !(p.sh.maxc == 1 && fp4)) {
     const int64_t items = G * p.npass * p.nb;
     const int64_t nkc = K / 256;
-    while (p.ksplit < 8 && items * p.ksplit * 2 <= 256 && nkc % (p.ksplit * 2) == 0 && nkc / (p.ksplit * 2) >= 2)
-      p.ksplit *= 2;
+    for (int s = 16; s >= 2; --s)
+      if (nkc % s == 0 && nkc / s >= 2 && items * s <= 256) {
+        p.ksplit = s;
+        break;
+      }
   }
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t nvfp4_grouped_linear_workspace_size(int64_t T, int64_t G, int64_t N, int64_t K) {
-  if (T <= 0 || G <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || T * G >= kMaxDim) return 0;
-  const GlPlan p = gl_plan(T, G, N, K);
-  const size_t part = p.ksplit > 1 ? round_up(sizeof(float) * (size_t)p.ksplit * T * G * N, 256) : 0;
-  return nvfp4_linear_workspace_size(T * G, N, K) + part;
+// Workspace: per-row shifts and the fp16 copy of bf16 activations, then the
+// fp32 partial sums of a K split.
+size_t staging_bytes(int64_t rows, int64_t K) {
+  return round_up(sizeof(int32_t) * (size_t)rows, 256) + round_up(sizeof(uint16_t) * (size_t)rows * K, 256);
 }
 
-int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
-                         const uint8_t* w_fp4, const uint8_t* w_sf, const float* ws2, int64_t T, int64_t G, int64_t N,
-                         int64_t K, void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+size_t gl_workspace(int64_t T, int64_t G, int64_t N, int64_t K) {
+  if (T <= 0 || G <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || T * G >= kMaxDim) return 0;
+  size_t worst = staging_bytes(T * G, K);
+  for (int fp4 = 0; fp4 < 2; ++fp4) {
+    const GlPlan p = gl_plan(T, G, N, K, fp4 != 0);
+    if (p.ksplit > 1)
+      worst = std::max(worst, staging_bytes(T * G, K) + round_up(sizeof(float) * (size_t)p.ksplit * T * G * N, 256));
+  }
+  return worst;
+}
+
+// The dense linear (G = 1) and the grouped linear: validation, then the launches.
+int gl_run(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa, const uint8_t* w_fp4,
+           const uint8_t* w_sf, const float* ws2, int64_t T, int64_t G, int64_t N, int64_t K, void* y_bf16,
+           void* workspace, size_t workspace_bytes, void* stream) {
   if (T < 0 || G <= 0 || N <= 0 || K <= 0 || T >= kMaxDim || G >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
     return NVFP4_ERR_SHAPE;
   if (K % 256 != 0 || N % 16 != 0 || T * G >= kMaxDim || G * N >= kMaxDim) return NVFP4_ERR_SHAPE;
@@ -252,16 +208,16 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
   if (fp4 && (!aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gsa, 4))) return NVFP4_ERR_ALIGN;
   if (!fp4 && !aligned(x_bf16, 16)) return NVFP4_ERR_ALIGN;
   const int64_t rows = T * G;   // activation rows of K: row t * G + g
-  const GlPlan plan = gl_plan(T, G, N, K);
+  const GlPlan plan = gl_plan(T, G, N, K, fp4);
   if (!fp4 || plan.ksplit > 1) {
-    if (!workspace || workspace_bytes < nvfp4_grouped_linear_workspace_size(T, G, N, K)) return NVFP4_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < gl_workspace(T, G, N, K)) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* wsp = static_cast<uint8_t*>(workspace);
   int* rowshift = reinterpret_cast<int*>(wsp);
   f16* x16 = fp4 ? nullptr : reinterpret_cast<f16*>(wsp + round_up(sizeof(int32_t) * (size_t)rows, 256));
-  float* part = plan.ksplit > 1 ? reinterpret_cast<float*>(wsp + nvfp4_linear_workspace_size(rows, N, K)) : nullptr;
+  float* part = plan.ksplit > 1 ? reinterpret_cast<float*>(wsp + staging_bytes(rows, K)) : nullptr;
   if (!fp4) {
     hipError_t e = launch_rows_to_f16(static_cast<const uint16_t*>(x_bf16), (int)rows, (int)K, rowshift, x16, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
@@ -293,6 +249,29 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
   g.part = part;
   if (launch_gemm(g, fp4 ? A_FP4 : A_F16, EPI_PART_F32, plan.sh, items, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
   return launch_status(launch_split_reduce(part, plan.ksplit, rows * N, static_cast<uint16_t*>(y_bf16), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) { return gl_workspace(M, 1, N, K); }
+
+int nvfp4_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
+                 const uint8_t* w_fp4, const uint8_t* w_sf, const float* gsb, int64_t M, int64_t N, int64_t K,
+                 void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return NVFP4_ERR_SHAPE;
+  return gl_run(x_bf16, x_fp4, x_sf, gsa, w_fp4, w_sf, gsb, M, 1, N, K, y_bf16, workspace, workspace_bytes, stream);
+}
+
+size_t nvfp4_grouped_linear_workspace_size(int64_t T, int64_t G, int64_t N, int64_t K) {
+  return gl_workspace(T, G, N, K);
+}
+
+int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const float* gsa,
+                         const uint8_t* w_fp4, const uint8_t* w_sf, const float* ws2, int64_t T, int64_t G, int64_t N,
+                         int64_t K, void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  return gl_run(x_bf16, x_fp4, x_sf, gsa, w_fp4, w_sf, ws2, T, G, N, K, y_bf16, workspace, workspace_bytes, stream);
 }
 
 size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared,

@@ -208,9 +208,9 @@ struct Frags {
   // the last chunk), both at once, so the row's 128 scale bytes of the group
   // are requested together; transpose4 of raw[f][h] then gives every lane its
   // word of chunks 8*sc+4h .. 8*sc+4h+3.
-  __device__ __forceinline__ void load_scales8(u32x4 (&raw)[R][2], int sc, int nkc, int lg) const {
-    const int k0 = min(8 * sc + lg, nkc - 1);
-    const int k1 = min(8 * sc + 4 + lg, nkc - 1);
+  __device__ __forceinline__ void load_scales8(u32x4 (&raw)[R][2], int sc, int nkc, int lg, int kbase = 0) const {
+    const int k0 = kbase + min(8 * sc + lg, nkc - 1);
+    const int k1 = kbase + min(8 * sc + 4 + lg, nkc - 1);
 #pragma unroll
     for (int f = 0; f < R; ++f) {
       // (down GEMM: with the non-temporal hint, measured 3% faster on MI355X;
@@ -413,7 +413,9 @@ void nvfp4_gemm_compact(const GemmArgs a) {
   Frags<R, EP> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
-  const int nkc = K / kChunk;
+  // chunks of this item: [kbase, kbase + nkc) (all of K unless K is split)
+  const int nkc = K / kChunk / (a.ksplit > 1 ? a.ksplit : 1);
+  const int kbase = it.ks * nkc;
   const int last = nkc - 1;
   const rsrc_t rb = make_rsrc(a.a, (uint32_t)a.a_rows * K * 2);
   const uint32_t vrow = (lane & 7) * fr.KB + (lane >> 3) * 16;   // whole-row code loads
@@ -442,8 +444,8 @@ void nvfp4_gemm_compact(const GemmArgs a) {
 
     u32x4 bq0a, bq0b, bq1a, bq1b;   // compact activation loads, two chunks in flight
     auto bload = [&](u32x4& x, u32x4& y, int kc) {
-      x = buf_load16(rb, vb0, kc * kChunk * 2);
-      if (two) y = buf_load16(rb, vb1, kc * kChunk * 2);
+      x = buf_load16(rb, vb0, (kbase + kc) * kChunk * 2);
+      if (two) y = buf_load16(rb, vb1, (kbase + kc) * kChunk * 2);
     };
     auto bstore = [&](uint8_t* slot, const u32x4& x, const u32x4& y) {
       *reinterpret_cast<u32x4*>(slot + wr0) = x;
@@ -473,11 +475,11 @@ void nvfp4_gemm_compact(const GemmArgs a) {
     };
 
     // prologue
-    fr.load_scales8(sraw, 0, nkc, lg);
+    fr.load_scales8(sraw, 0, nkc, lg, kbase);
     bload(bq0a, bq0b, 0);
     bload(bq1a, bq1b, min(1, last));
-    fr.load_codes_rows(wc0a, wc1a, vrow, 0);
-    fr.load_codes_rows(wc0b, wc1b, vrow, min(1, last));
+    fr.load_codes_rows(wc0a, wc1a, vrow, kbase);
+    fr.load_codes_rows(wc0b, wc1b, vrow, kbase + min(1, last));
     bstore(slot0, bq0a, bq0b);
     bload(bq0a, bq0b, min(2, last));
 
@@ -493,19 +495,19 @@ void nvfp4_gemm_compact(const GemmArgs a) {
           transpose4(scur[f][h]);
         }
       }
-      fr.load_scales8(sraw, kc / 8 + 1, nkc, lg);
+      fr.load_scales8(sraw, kc / 8 + 1, nkc, lg, kbase);
 #pragma unroll
       for (int c8 = 0; c8 < 8; ++c8) {
         const int k = kc + c8;
         if (k >= nkc) break;
         if ((c8 & 1) == 0) {
           compute(wc0a, wc1a, slot0, c8);
-          fr.load_codes_rows(wc0a, wc1a, vrow, min(k + 2, last));
+          fr.load_codes_rows(wc0a, wc1a, vrow, kbase + min(k + 2, last));
           bstore(slot1, bq1a, bq1b);
           bload(bq1a, bq1b, min(k + 3, last));
         } else {
           compute(wc0b, wc1b, slot1, c8);
-          fr.load_codes_rows(wc0b, wc1b, vrow, min(k + 2, last));
+          fr.load_codes_rows(wc0b, wc1b, vrow, kbase + min(k + 2, last));
           bstore(slot0, bq0a, bq0b);
           bload(bq0a, bq0b, min(k + 3, last));
         }
@@ -1011,8 +1013,8 @@ hipError_t launch_gemm(const GemmArgs& a, int amode, int epi, GemmShape sh, int 
   if (amode == A_F16 && epi == EPI_SLOT) return dispatch<A_F16, EPI_SLOT>(a, sh, n_groups, s);
   if (amode == A_FP4 && epi == EPI_SLOT) return dispatch<A_FP4, EPI_SLOT>(a, sh, n_groups, s);
   if (epi == EPI_PART_F32) {
-    // K splits run on the four-wave LDS kernel only
-    if (sh.maxc == 1 || sh.nw != kNW || a.ksplit < 1) return hipErrorInvalidValue;
+    // K splits run on the four-wave LDS kernel and the compact kernel
+    if (sh.nw != kNW || a.ksplit < 1 || (sh.maxc == 1 && amode != A_F16)) return hipErrorInvalidValue;
     if (amode == A_F16) return dispatch<A_F16, EPI_PART_F32>(a, sh, n_groups, s);
     if (amode == A_FP4) return dispatch<A_FP4, EPI_PART_F32>(a, sh, n_groups, s);
   }
