@@ -11,29 +11,28 @@
 // global scale).
 //
 // Common mapping:
-//  * a work item is (group, block of weight rows); groups come from a
-//    device-side list sorted by size, so no host synchronisation is needed.
-//    Groups with more than 16 rows go to the LDS kernel, the others to the
-//    direct kernel (two launches over the two parts of the list);
-//  * every wave owns R fragments of 16 weight rows and streams them over the
-//    whole K range once per pass of activation rows;
+//  * a work item is (group, block of weight rows); MoE groups come from a
+//    device-side list sorted by size, so no host synchronisation is needed:
+//    groups of more than 4 rows go to the LDS kernel, the others to the
+//    barrier-free kernels (two launches over the two parts of the list).  The
+//    dense and grouped linear have fixed groups; their work items also carry
+//    a pass of rows and, when they are few, a part of a split K range;
+//  * every wave owns R fragments of 16 weight rows and streams them over its
+//    K range once per pass of activation rows;
 //  * K is walked in chunks of 256.  Lane (r, g) of a fragment (r = lane%16,
-//    g = lane/16) loads bytes [32g, 32g+32) of the chunk of row r (64 codes)
-//    with two 16-byte loads, and the 4 scale bytes of those 4 blocks.  MFMA
-//    step q (0..7) covers K positions {64g' + 8q + e}: the MFMA's K index is a
-//    permutation of the real K, the same for both operands, so the sum is
-//    unchanged.  (Measured on MI355X: this pattern streams at ~6 TB/s; wider
-//    per-lane spans coalesce worse.)
+//    g = lane/16) holds bytes [32g, 32g+32) of the chunk of row r (64 codes)
+//    and the 4 scale bytes of those 4 blocks.  MFMA step q (0..7) covers K
+//    positions {64g' + 8q + e}: the MFMA's K index is a permutation of the
+//    real K, the same for both operands, so the sum is unchanged;
 //  * weights are the MFMA A operand (16 weight rows), activations the B
 //    operand (16 rows of tokens): D[weight row][token row];
 //  * activations arrive as fp16 rows (bf16 / fp32 values scaled by a per-row
 //    power of two into [2^14, 2^15), undone in the epilogue: exact) or as
 //    NVFP4 rows (decoded exactly; global scale in the epilogue).
 //
-// Direct kernel (groups of <= 16 rows, the decode case): no LDS and no
-// barriers.  Each lane also loads its own B fragment (the token row it holds
-// in the MFMA layout) from global memory, two chunks ahead like the weights,
-// so every wave streams independently.
+// Compact kernel (groups of at most 4 rows, fp16 activations: the decode
+// case) and direct kernel (the same with NVFP4 activations): no barriers;
+// every wave streams its weights independently, two chunks ahead.
 //
 // LDS kernel (bigger groups): the workgroup stages the activation chunk
 // [16*MAXC rows, 256] into LDS (double buffered) and every wave reads its B
@@ -384,7 +383,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
 // compact kernel: fp16 activations, at most kSmallRows rows per pass
 // ---------------------------------------------------------------------------
 //
-// Per 256-K chunk a wave issues 2 code loads per fragment, 1/4 scale load per
+// Per 256-K chunk a wave issues 2 code loads per fragment (8 whole rows each,
+// non-temporal, then a lane-pair swap into the MFMA layout), 1/4 scale load per
 // fragment (the scales of 8 chunks come with two loads per fragment issued
 // together, so each weight row's 128 scale bytes of the group are fetched
 // once; transposed across lane groups) and ceil(rows/2) activation loads:
@@ -392,7 +392,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
 // activation rows go through a wave-private LDS slot (LDS operations of one
 // wave complete in order, so no barrier is needed) and are read back in the
 // MFMA layout; lanes of absent rows read row 0 (their columns are
-// discarded).  Activations are loaded two chunks ahead, weights two chunks
+// discarded).  Activations are loaded three chunks ahead, weights two chunks
 // ahead, scales one 8-chunk group ahead.
 
 constexpr int kSmallRows = 4;
