@@ -1,5 +1,6 @@
 """Plain, slow CPU oracle for the NVFP4 block-scaled linear, the grouped linear of the
-attention output projection, the router gate and the MoE grouped GEMM.
+attention output projection, the router gate, the fused RMSNorm + quantization and the
+MoE grouped GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
