@@ -45,6 +45,9 @@ WORKLOADS = {
     # router gate (FP8 round-tripped bf16 weight, top-8 softmax) at the decode and large-batch token counts
     "router_decode": dict(kind="router", T=64, H=7168, E=384, k=8),
     "router_4096": dict(kind="router", T=4096, H=7168, E=384, k=8),
+    # RMSNorm fused with the NVFP4 activation quantization (feeds the q_a / kv projections)
+    "rmsnorm_quant_decode": dict(kind="rmsnorm_quant", T=64, K=7168),
+    "rmsnorm_quant_4096": dict(kind="rmsnorm_quant", T=4096, K=7168),
     # attention output projection wo_a: 8 groups of K 4096, output width 1024 per group
     "wo_a_decode": dict(kind="grouped_linear", T=64, G=8, N=1024, K=4096),
     "wo_a_4096": dict(kind="grouped_linear", T=4096, G=8, N=1024, K=4096),
@@ -557,6 +560,90 @@ def run_grouped_linear(args, cfg):
     }
 
 
+def run_rmsnorm_quant(args, cfg):
+    """RMSNorm fused with the NVFP4 quantizer (one nvfp4_rmsnorm_quantize call,
+    global scale computed), timed beside the unfused path it must equal: the
+    RMSNorm pass writing bf16 y, then nvfp4_quantize_act on y."""
+    import torch
+
+    from fp4_block_scaled_route_amd import ops, synth
+
+    t, k = cfg["T"], cfg["K"]
+    eps = 1e-6
+    copies = max(1, min(16, int(1.0e9 // (t * k * 2))))   # rotate inputs past the last-level cache
+    xs = [synth.bf16_normal((t, k), args.seed + i).cuda() for i in range(copies)]
+    w = (synth.bf16_normal((k,), args.seed + 999).float() * 0.5 + 1.0).to(torch.bfloat16).cuda()
+    q = torch.empty((t, k // 2), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((t, k // 16), dtype=torch.uint8, device="cuda")
+    gs = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y = torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
+    work = torch.empty(max(16, ops.lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8, device="cuda")
+    L = ops.lib()
+    s = torch.cuda.current_stream().cuda_stream
+
+    def fused(i):
+        ops._check(L.nvfp4_rmsnorm_quantize(xs[i % copies].data_ptr(), w.data_ptr(), eps, t, k, None,
+                                            gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), work.data_ptr(),
+                                            work.numel(), s))
+
+    def unfused(i):
+        ops._check(L.nvfp4_rmsnorm_quantize(xs[i % copies].data_ptr(), w.data_ptr(), eps, t, k, y.data_ptr(),
+                                            gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), work.data_ptr(),
+                                            work.numel(), s))
+        ops._check(L.nvfp4_quantize_act(y.data_ptr(), t, k, gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), s))
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(args.steps):
+            fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    ms = timed(fused)
+    ms_unfused = timed(unfused)
+    nbytes = t * k * 2 + k * 2 + t * (k // 2) + t * (k // 16) + 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import rmsnorm
+        log("timing the CPU oracle on a bounded sample ...")
+        rows = min(t, 64)
+        xh = xs[0][:rows].float().cpu().numpy()
+        wh = w.float().cpu().numpy()
+        t_start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t_start < 10.0:
+            rmsnorm.rmsnorm_quantize(xh, wh, eps)
+            reps += 1
+        sec = (time.perf_counter() - t_start) / reps
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        sample_bytes = rows * k * 2 + k * 2 + rows * (k // 2) + rows * (k // 16) + 4
+        cpu = dict(value=round(sample_bytes / sec / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                   sample=f"{rows} rows of {k}, float32/float64 numpy oracle, {reps} repetitions in about 10 s")
+    return {
+        "metric": "RMSNorm + NVFP4 quantization GB/s (%roofline), 1xMI355X",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"RMSNorm of x [{t}, {k}] bf16 with a bf16 weight, fused with the NVFP4 quantizer "
+                               f"(global scale computed), {copies} rotating inputs", "name": args.workload},
+        "unfused_ms": round(ms_unfused, 5),
+        "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                         kernel="nvfp4_rmsnorm_stats + nvfp4_rmsnorm_quant (one call)", kernel_ms=round(ms, 5),
+                         algorithmic_bytes_per_launch=nbytes),
+        "cpu_baseline": cpu,
+    }
+
+
 def run_copy(args):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE readings to bytes."""
@@ -598,7 +685,7 @@ def main():
         return
     cfg = WORKLOADS[args.workload]
     run = {"moe": run_moe, "linear": run_linear, "router": run_router,
-           "grouped_linear": run_grouped_linear}[cfg["kind"]]
+           "grouped_linear": run_grouped_linear, "rmsnorm_quant": run_rmsnorm_quant}[cfg["kind"]]
     res = run(args, cfg)
     print(json.dumps(res), flush=True)
 

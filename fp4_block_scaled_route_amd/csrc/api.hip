@@ -274,6 +274,29 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
   return gl_run(x_bf16, x_fp4, x_sf, gsa, w_fp4, w_sf, ws2, T, G, N, K, y_bf16, workspace, workspace_bytes, stream);
 }
 
+size_t nvfp4_rmsnorm_quantize_workspace_size(int64_t T) {
+  if (T <= 0 || T >= kMaxDim) return 0;
+  return round_up(sizeof(float) * (size_t)T, 256);
+}
+
+int nvfp4_rmsnorm_quantize(const void* x_bf16, const void* w_bf16, float eps, int64_t T, int64_t K, void* y_bf16,
+                           float* gs, int compute_gs, uint8_t* x_fp4, uint8_t* x_sf, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (T < 0 || K <= 0 || K % 16 != 0 || T >= kMaxDim || K >= kMaxDim || T * K >= kMaxDim) return NVFP4_ERR_SHAPE;
+  if (!(eps > 0.0f) || eps == __builtin_inff()) return NVFP4_ERR_ARG;
+  if (T == 0) return NVFP4_OK;
+  if (!x_bf16 || !w_bf16 || !gs || !x_fp4 || !x_sf) return NVFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w_bf16, 16) || !aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gs, 4) ||
+      (y_bf16 && !aligned(y_bf16, 16)))
+    return NVFP4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < nvfp4_rmsnorm_quantize_workspace_size(T)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  return launch_status(launch_rmsnorm_quantize(static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w_bf16),
+                                               eps, (int)T, (int)K, static_cast<uint16_t*>(y_bf16), gs, compute_gs,
+                                               x_fp4, x_sf, static_cast<float*>(workspace),
+                                               static_cast<hipStream_t>(stream)));
+}
+
 size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared,
                                 int h_fp4) {
   if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;

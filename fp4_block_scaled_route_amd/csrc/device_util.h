@@ -84,6 +84,32 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
 // Power-of-two shift that maps a row whose max |value| has the fp32 bit
 // pattern `mbits` into [2^14, 2^15): exact fp16 staging of bf16/fp32 rows.
 // Zero rows, and rows whose max is inf/NaN, get shift 0.
+// NVFP4 quantization of one 16-element block with global scale gs (every step
+// one correctly rounded fp32 operation, in this order): scale byte =
+// RNE_E4M3(amax_blk / (6 * gs)); codes = RNE_E2M1(x * (1 / (E4M3(byte) * gs)))
+// packed two per byte, element 2j in the low nibble.  gs == 0 or a zero scale
+// gives zero codes.  Returns the scale byte.
+__device__ __forceinline__ uint32_t quant_block16(const float (&xv)[16], float gs, uint2& packed) {
+  float ab = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ab = fmaxf(ab, __builtin_fabsf(xv[e]));
+  uint32_t sbyte = 0;
+  packed = make_uint2(0u, 0u);
+  if (gs != 0.0f) {
+    sbyte = e4m3_encode_nonneg(ab / (6.0f * gs));
+    const float scale = e4m3_to_float(sbyte) * gs;
+    if (scale != 0.0f) {
+      const float r = 1.0f / scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        packed.x |= e2m1_encode(xv[e] * r) << (4 * e);
+        packed.y |= e2m1_encode(xv[8 + e] * r) << (4 * e);
+      }
+    }
+  }
+  return sbyte;
+}
+
 __device__ __forceinline__ int shift_from_maxbits(uint32_t mbits) {
   const uint32_t e = (mbits >> 23) & 0xFFu;
   if (mbits == 0u || e == 0xFFu) return 0;

@@ -147,6 +147,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 // y[i] = bf16(sum over s = 0..S-1, in that order, of part[s * n + i]), n % 4 == 0.
 hipError_t launch_split_reduce(const float* part, int S, int64_t n, uint16_t* y, hipStream_t stream);
 
+// Fused RMSNorm + NVFP4 quantization of x [T, K] with weight w [K]: r per row
+// into rrow [T], y [T, K] bf16 if y != nullptr, codes q [T, K/2], scale bytes
+// sf [T, K/16]; gs computed (compute_gs) or read from *gs.
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* w, float eps, int T, int K, uint16_t* y,
+                                   float* gs, int compute_gs, uint8_t* q, uint8_t* sf, float* rrow,
+                                   hipStream_t stream);
+
 // word = max |x| over n bf16 values (n % 8 == 0), as a float (zeroed first).
 hipError_t launch_bf16_amax(const uint16_t* x, int64_t n, float* word, hipStream_t stream);
 

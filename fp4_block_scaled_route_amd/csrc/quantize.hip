@@ -61,27 +61,13 @@ __global__ __launch_bounds__(256) void nvfp4_quant_blocks(const uint16_t* x, int
   const uint4 v0 = src[0], v1 = src[1];
   const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   float xv[16];
-  float ab = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     xv[2 * e] = bf16_bits_to_float(u[e] & 0xFFFFu);
     xv[2 * e + 1] = bf16_bits_to_float(u[e] >> 16);
-    ab = fmaxf(ab, fmaxf(__builtin_fabsf(xv[2 * e]), __builtin_fabsf(xv[2 * e + 1])));
   }
-  uint32_t sbyte = 0;
-  uint2 packed = make_uint2(0u, 0u);
-  if (gs != 0.0f) {
-    sbyte = e4m3_encode_nonneg(ab / (6.0f * gs));
-    const float scale = e4m3_to_float(sbyte) * gs;
-    if (scale != 0.0f) {
-      const float r = 1.0f / scale;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        packed.x |= e2m1_encode(xv[e] * r) << (4 * e);
-        packed.y |= e2m1_encode(xv[8 + e] * r) << (4 * e);
-      }
-    }
-  }
+  uint2 packed;
+  const uint32_t sbyte = quant_block16(xv, gs, packed);
   reinterpret_cast<uint2*>(q)[b] = packed;
   sf[b] = (uint8_t)sbyte;
 }

@@ -23,6 +23,8 @@ EXPORTED = (
     "nvfp4_status_string",
     "nvfp4_abi_version",
     "nvfp4_quantize_act",
+    "nvfp4_rmsnorm_quantize_workspace_size",
+    "nvfp4_rmsnorm_quantize",
     "nvfp4_linear_workspace_size",
     "nvfp4_linear",
     "nvfp4_grouped_linear_workspace_size",
@@ -77,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_abi_version.argtypes = []
         L.nvfp4_quantize_act.restype = ctypes.c_int
         L.nvfp4_quantize_act.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr]
+        L.nvfp4_rmsnorm_quantize_workspace_size.restype = ctypes.c_size_t
+        L.nvfp4_rmsnorm_quantize_workspace_size.argtypes = [_c_i64]
+        L.nvfp4_rmsnorm_quantize.restype = ctypes.c_int
+        L.nvfp4_rmsnorm_quantize.argtypes = [_c_ptr, _c_ptr, ctypes.c_float, _c_i64, _c_i64, _c_ptr, _c_ptr,
+                                             ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]
         L.nvfp4_linear_workspace_size.restype = ctypes.c_size_t
         L.nvfp4_linear_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64]
         L.nvfp4_linear.restype = ctypes.c_int
@@ -143,6 +150,25 @@ def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
         gsb = gs
     _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _stream()))
     return q, sf, gsb
+
+
+def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, gs: Optional[torch.Tensor] = None,
+                     y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """RMSNorm of bf16 rows x [T, K] with weight w [K], quantized to NVFP4.
+    Returns (codes [T, K/2], scale bytes [T, K/16], gs [1]); gs is computed
+    unless given; ``y`` (bf16 [T, K]) receives the RMSNorm output if given."""
+    t, k = x.shape
+    dev = x.device
+    q = torch.empty((t, k // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty((t, k // 16), dtype=torch.uint8, device=dev)
+    compute = gs is None
+    g = torch.zeros(1, dtype=torch.float32, device=dev) if compute else gs
+    if workspace is None:
+        workspace = torch.empty(max(16, lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().nvfp4_rmsnorm_quantize(_p(x), _p(w), float(eps), t, k, _p(y), _p(g), int(compute), _p(q), _p(sf),
+                                        _p(workspace), wsb, _stream()))
+    return q, sf, g
 
 
 def linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Optional[torch.Tensor] = None,

@@ -90,6 +90,26 @@ int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int 
                        uint8_t* x_fp4, uint8_t* x_sf, void* stream);
 
 /*
+ * nvfp4_rmsnorm_quantize - RMSNorm fused with nvfp4_quantize_act (page
+ * "commit 1121cd7 - single_shot_inference.py", the notes on the A/B
+ * comparison of the fused "P4" RMSNorm + quantization against the unfused
+ * path): the result is exactly that of RMSNorm followed by the quantizer.
+ *   RMSNorm of each row of x_bf16 [T, K] with weight w_bf16 [K]:
+ *     r = fp32(1 / sqrt(sum_k x^2 / K + eps))   (sum, root and quotient in fp64)
+ *     y = bf16_RNE(fp32(fp32(x * r) * w))
+ *   y_bf16 [T, K]: optional output of y (NULL: not written).
+ *   gs, compute_gs, x_fp4 [T, K/2], x_sf [T, K/16]: as nvfp4_quantize_act,
+ *   applied to y.
+ *   workspace: nvfp4_rmsnorm_quantize_workspace_size(T) bytes (r per row).
+ * Requires K % 16 == 0 (K % 256 == 0 to feed nvfp4_linear), eps > 0 and
+ * finite (NVFP4_ERR_ARG otherwise), 16-byte aligned tensors.
+ */
+size_t nvfp4_rmsnorm_quantize_workspace_size(int64_t T);
+int nvfp4_rmsnorm_quantize(const void* x_bf16, const void* w_bf16, float eps, int64_t T, int64_t K, void* y_bf16,
+                           float* gs, int compute_gs, uint8_t* x_fp4, uint8_t* x_sf, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_linear - dense NVFP4 linear, y[M, N] = x[M, K] @ W[N, K]^T, bf16 out,
  * fp32 accumulation (page "commit 1121cd7", the GEMM statement in the note on
  * the weight-dequant global scale; the NVFP4 linear layer of page

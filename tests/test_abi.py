@@ -89,6 +89,26 @@ def test_grouped_linear_validation(lib):
     assert call(args(wb=ws - 1)) == -4
 
 
+def test_rmsnorm_quantize_validation(lib):
+    L = lib
+    ws = L.nvfp4_rmsnorm_quantize_workspace_size(64)
+    assert ws >= 64 * 4
+
+    def call(x=FAKE, w=FAKE, eps=1e-6, T=64, K=7168, y=None, gs=FAKE, comp=1, q=FAKE, sf=FAKE, work=FAKE, wb=ws):
+        return L.nvfp4_rmsnorm_quantize(x, w, eps, T, K, y, gs, comp, q, sf, work, wb, None)
+    assert call(K=100) == -2                 # K not a multiple of 16
+    assert call(T=-1) == -2
+    assert call(eps=0.0) == -6               # eps must be positive
+    assert call(eps=float("nan")) == -6
+    assert call(T=0) == 0
+    assert call(w=None) == -1
+    assert call(gs=None) == -1
+    assert call(x=ctypes.c_void_p(0x1008)) == -3
+    assert call(y=ctypes.c_void_p(0x1004)) == -3
+    assert call(work=None) == -4
+    assert call(wb=ws - 1) == -4
+
+
 def test_quantize_validation(lib):
     L = lib
     assert L.nvfp4_quantize_act(FAKE, 4, 40, FAKE, 1, FAKE, FAKE, None) == -2
