@@ -204,7 +204,10 @@ def moe_accounting(cfg, st):
     step_bytes = w_bytes + act_in + out
     row_bytes = (h // 2 + h // 16) if cfg["fp4"] else h * 2   # activation row as the GEMM reads it
     launches = {}
-    for name, sel in (("big", counts > SMALL_GROUP_ROWS), ("small", (counts > 0) & (counts <= SMALL_GROUP_ROWS))):
+    # more than 16 rows per group on average: one launch of the LDS kernel over all groups
+    large_batch = pairs / len(counts) > 16
+    big_sel = counts > 0 if large_batch else counts > SMALL_GROUP_ROWS
+    for name, sel in (("big", big_sel), ("small", (counts > 0) & ~big_sel)):
         m = counts[sel]
         launches[name] = dict(groups=int(sel.sum()), rows=int(m.sum()),
                               bytes=int(sel.sum()) * BYTES_PER_EXPERT_W1 + int(m.sum()) * row_bytes,

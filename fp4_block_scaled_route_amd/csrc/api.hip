@@ -369,6 +369,15 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
     GemmShape small{1, r, 4};
     const int half = epi == EPI_SWIGLU_F32 || epi == EPI_SWIGLU_FP4 ? 2 : 1;
     ev(ev_big);
+    if (large_batch) {
+      // groups of at most 4 rows are rare here: all groups go to the LDS
+      // kernel (it takes any row count), so no launch runs empty
+      g.list_part = 2;
+      g.nb = (int)((g.N / half + gemm_rows_per_block(epi, big) - 1) / gemm_rows_per_block(epi, big));
+      if (launch_gemm(g, amode, epi, big, G, s) != hipSuccess) return false;
+      ev(ev_small);
+      return true;
+    }
     g.list_part = 0;
     g.nb = (int)((g.N / half + gemm_rows_per_block(epi, big) - 1) / gemm_rows_per_block(epi, big));
     if (launch_gemm(g, amode, epi, big, n_big_max, s) != hipSuccess) return false;

@@ -14,7 +14,9 @@
 //  * a work item is (group, block of weight rows); MoE groups come from a
 //    device-side list sorted by size, so no host synchronisation is needed:
 //    groups of more than 4 rows go to the LDS kernel, the others to the
-//    barrier-free kernels (two launches over the two parts of the list).  The
+//    barrier-free kernels (two launches over the two parts of the list; at
+//    large batches, averaging more than 16 rows per group, one launch of the
+//    LDS kernel over the whole list).  The
 //    dense and grouped linear have fixed groups; their work items also carry
 //    a pass of rows and, when they are few, a part of a split K range;
 //  * every wave owns R fragments of 16 weight rows and streams them over its

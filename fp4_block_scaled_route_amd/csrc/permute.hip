@@ -33,8 +33,58 @@ constexpr int kMaxExperts = 512;
 // One wave per row: max |x| of the bf16 row, the power-of-two shift that maps
 // it into [2^14, 2^15), and the fp16 copy of the row scaled by that power of
 // two (exact: bf16 values have 8 significant bits), stored step-major.
+//
+// Rows of at most NV * 512 elements are read once, all loads of the row
+// issued together and held in registers (one memory round trip per row);
+// longer rows are read twice, 512 elements per step.
+template <int NV>
+__device__ void rows_to_f16_held(const uint16_t* x, int rows, int cols, int* rowshift, f16* x16, int first_wave,
+                                 int wave_stride) {
+  const int lane = threadIdx.x & 63;
+  for (int r = first_wave; r < rows; r += wave_stride) {
+    const uint16_t* row = x + (int64_t)r * cols;
+    uint4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (lane + 64 * i) * 8;
+      v[i] = c < cols ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx = max(mx, u[e] & 0x7FFFu);
+        mx = max(mx, (u[e] >> 16) & 0x7FFFu);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    const int sh = shift_from_maxbits(mx << 16);
+    if (lane == 0) rowshift[r] = sh;
+    f16* out = x16 + (int64_t)r * cols;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (lane + 64 * i) * 8;
+      if (c >= cols) continue;
+      const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = (f16)__builtin_ldexpf(bf16_bits_to_float(u[e] & 0xFFFFu), sh);
+        o[2 * e + 1] = (f16)__builtin_ldexpf(bf16_bits_to_float(u[e] >> 16), sh);
+      }
+      *reinterpret_cast<f16x8*>(out + step_major_pos(c)) = o;
+    }
+  }
+}
+
 __device__ void rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift, f16* x16, int first_wave,
                             int wave_stride) {
+  if (cols <= 4 * 512) return rows_to_f16_held<4>(x, rows, cols, rowshift, x16, first_wave, wave_stride);
+  if (cols <= 8 * 512) return rows_to_f16_held<8>(x, rows, cols, rowshift, x16, first_wave, wave_stride);
+  if (cols <= 16 * 512) return rows_to_f16_held<16>(x, rows, cols, rowshift, x16, first_wave, wave_stride);
   const int lane = threadIdx.x & 63;
   for (int r = first_wave; r < rows; r += wave_stride) {
     const uint16_t* row = x + (int64_t)r * cols;

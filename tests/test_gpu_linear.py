@@ -19,6 +19,8 @@ def _run_bf16(li):
     (1, 1536, 7168), (32, 1536, 7168), (128, 1536, 7168),   # projection shape
     (1, 24576, 1536), (32, 24576, 1536), (128, 24576, 1536),
     (17, 48, 512), (100, 64, 256), (129, 32, 768),      # ragged token counts (several passes)
+    (3, 96, 2304), (2, 64, 8448),                       # bf16 staging: 8 loads per lane (partly masked);
+                                                        # rows longer than 8192 (read twice)
 ])
 def test_linear_bf16(m, n, k):
     say(f"linear bf16 M={m} N={n} K={k}")

@@ -119,6 +119,49 @@ def test_moe_small_fully_fp4_and_calibration():
     compare(y, ref, what="fully fp4 small")
 
 
+@pytest.mark.parametrize("t,h,i,e,k,seed", [
+    (160, 1024, 1024, 24, 4, 11),   # K multiple of 1024: eight-wave kernel for both GEMMs
+    (150, 512, 256, 20, 3, 12),     # four-wave large-batch configuration
+])
+def test_moe_large_batch_with_tiny_groups(t, h, i, e, k, seed):
+    """More than 16 rows per group on average sends every group, including
+    groups of 1-4 rows, to the LDS kernel in one launch; hot groups take
+    several passes.  Zipf(1.6) routing gives both."""
+    say(f"moe large batch with tiny groups T={t} H={h} I={i} E={e} k={k}")
+    mi = synth.make_moe(t, h, i, e, k, seed=seed, routing="zipf", zipf_s=1.6, shared=True, threads=4)
+    counts = np.bincount(mi.topk_ids.ravel(), minlength=e)
+    assert (t * k + t) / (e + 1) > 16 and ((counts > 0) & (counts <= 4)).any() and counts.max() > 128
+    de, ds = DeviceExperts(mi.experts), DeviceExperts(mi.shared)
+    y, off, perm = _run(de, mi.topk_ids, mi.topk_w, x=dev(mi.x), shared=ds)
+    _check_perm(mi.topk_ids, e, True, off, perm)
+    ref = _oracle(synth.bf16_to_float64(mi.x), mi.topk_ids, mi.topk_w, mi.experts, mi.shared, None)
+    compare(y, ref, what="large batch, tiny groups")
+
+
+def test_moe_fully_fp4_large_batch_with_tiny_groups():
+    """The fully-FP4 path on the eight-wave kernel with groups of 1-4 rows and
+    groups of more than one 112-row pass."""
+    t, h, i, e, k = 192, 1024, 1024, 24, 4
+    say("moe fully fp4 large batch with tiny groups")
+    mi = synth.make_moe(t, h, i, e, k, seed=13, routing="zipf", zipf_s=1.6, shared=False, threads=4)
+    counts = np.bincount(mi.topk_ids.ravel(), minlength=e)
+    assert ((counts > 0) & (counts <= 4)).any() and counts.max() > 112
+    de = DeviceExperts(mi.experts)
+    xq, xs, gs = ops.quantize_act(dev(mi.x))
+    rq, rs, rgs = quant.quantize_nvfp4(mi.x.float().numpy())
+    xa = quant.dequantize_nvfp4(rq, rs, rgs)
+    amax = 0.0
+    for tt in range(t):
+        for j in range(k):
+            ex = mi.experts.expert(int(mi.topk_ids[tt, j]))
+            amax = max(amax, moe.hidden_amax(xa[tt:tt + 1], codec.dequant_nvfp4(*ex[:3])))
+    a2 = np.float32(np.float32(amax) / np.float32(2688.0))
+    y, off, perm = _run(de, mi.topk_ids, mi.topk_w, x_fp4=xq, x_sf=xs, a1_gs=gs, a2_gs=f32(a2))
+    _check_perm(mi.topk_ids, e, False, off, perm)
+    ref = _oracle(xa, mi.topk_ids, mi.topk_w, mi.experts, None, None, a2_gs=a2)
+    compare(y, ref, what="fully fp4, tiny groups")
+
+
 # ---------------------------------------------------------------------------
 # full DeepSeek-V4-shaped configurations, sampled tokens
 # ---------------------------------------------------------------------------
