@@ -28,7 +28,7 @@ int pick_maxc(double rows_per_group) {
 
 // Workspace layout of nvfp4_moe_grouped.
 struct MoeLayout {
-  size_t offsets, glist, gcount, perm, inv, rowshift, x16, hmax, hshift, h, h16, hq, hq_sf, slot, total;
+  size_t offsets, glist, gcount, perm, inv, bcnt, rowshift, x16, hmax, hshift, h, h16, hq, hq_sf, slot, total;
 };
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared, int h_fp4) {
@@ -42,6 +42,7 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, i
   L.gcount = take(sizeof(int32_t) * 2);
   L.perm = take(sizeof(int32_t) * Pt);
   L.inv = take(sizeof(int32_t) * Pt);
+  L.bcnt = take(sizeof(int32_t) * (size_t)permute_blocks(T * topk) * E);
   L.rowshift = take(sizeof(int32_t) * T);
   L.x16 = take(sizeof(uint16_t) * (size_t)T * H);
   L.hmax = take(sizeof(uint32_t) * Pt);
@@ -408,7 +409,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   pa.x16 = x16;
   pa.zero_buf = h_fp4 ? nullptr : hmax;
   pa.n_zero = Pt;
-  if (launch_permute(pa, s) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  if (launch_permute(pa, reinterpret_cast<int*>(ws + L.bcnt), s) != hipSuccess) return NVFP4_ERR_LAUNCH;
 
   // 2. gate/up GEMM with fused SwiGLU
   GemmArgs g1{};

@@ -10,32 +10,56 @@
 
 namespace nvfp4 {
 
+// KMAX > 0 (topk <= KMAX): all row loads of the token are issued before the
+// first use, so a wave has topk + 1 requests in flight instead of one; the
+// sum still runs in the order j = 0..topk-1, then the shared row.  KMAX == 0:
+// any topk, one row at a time.
+template <int KMAX>
 __global__ __launch_bounds__(256) void nvfp4_moe_combine(const CombineArgs a) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (n >= a.H) return;
   const int P = a.T * a.topk;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.topk; ++j) {
-    const int id = a.ids[t * a.topk + j];
-    if (id < 0 || id >= a.E) continue;
-    const float w = a.w[t * a.topk + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n);
+  auto add = [&](const uint4 v, float w) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += w * bf16_bits_to_float(u[i] & 0xffffu);
       acc[2 * i + 1] += w * bf16_bits_to_float(u[i] >> 16);
     }
-  }
-  if (a.shared) {
-    const uint4 v = *reinterpret_cast<const uint4*>(a.slot + (int64_t)(P + t) * a.H + n);
+  };
+  auto add_shared = [&](const uint4 v) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += bf16_bits_to_float(u[i] & 0xffffu);
       acc[2 * i + 1] += bf16_bits_to_float(u[i] >> 16);
     }
+  };
+  if constexpr (KMAX > 0) {
+    uint4 v[KMAX];
+    bool ok[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int id = j < a.topk ? a.ids[t * a.topk + j] : -1;
+      ok[j] = id >= 0 && id < a.E;
+      v[j] = ok[j] ? *reinterpret_cast<const uint4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n)
+                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint4 vs = make_uint4(0u, 0u, 0u, 0u);
+    if (a.shared) vs = *reinterpret_cast<const uint4*>(a.slot + (int64_t)(P + t) * a.H + n);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (ok[j]) add(v[j], a.w[t * a.topk + j]);
+    if (a.shared) add_shared(vs);
+  } else {
+    for (int j = 0; j < a.topk; ++j) {
+      const int id = a.ids[t * a.topk + j];
+      if (id < 0 || id >= a.E) continue;
+      add(*reinterpret_cast<const uint4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n), a.w[t * a.topk + j]);
+    }
+    if (a.shared) add_shared(*reinterpret_cast<const uint4*>(a.slot + (int64_t)(P + t) * a.H + n));
   }
   uint4 o;
   o.x = float_to_bf16_bits(acc[0]) | (float_to_bf16_bits(acc[1]) << 16);
@@ -47,7 +71,10 @@ __global__ __launch_bounds__(256) void nvfp4_moe_combine(const CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   dim3 grid((a.H / 8 + 255) / 256, a.T);
-  hipLaunchKernelGGL(nvfp4_moe_combine, grid, dim3(256), 0, s, a);
+  if (a.topk <= 8)
+    hipLaunchKernelGGL(nvfp4_moe_combine<8>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(nvfp4_moe_combine<0>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -124,7 +124,10 @@ struct PermuteArgs {
   unsigned* zero_buf;  // [n_zero] set to 0, or nullptr
   int n_zero;
 };
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+// Workgroups of the multi-workgroup permutation for P pairs (0: one
+// workgroup does it all); it needs bcnt[blocks * E] ints of workspace.
+int permute_blocks(int64_t P);
+hipError_t launch_permute(const PermuteArgs& a, int* bcnt, hipStream_t stream);
 
 // fp16 copy of bf16 rows scaled by per-row powers of two (rowshift[r]).
 hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift, f16* x16,

@@ -6,21 +6,26 @@
 // grouped by expert id, stable in f; the shared expert's group of T rows
 // follows the routed groups.
 //
-// One workgroup of 16 waves does the whole permutation (P = T*topk pairs is
-// at most a few tens of thousands):
-//   1. wave w counts the ids of its contiguous segment of pairs into its own
+// A workgroup of 16 waves ranks a contiguous range of the pairs:
+//   1. wave w counts the ids of its contiguous piece of the range into its own
 //      LDS histogram row (LDS atomics: order-free, exact);
 //   2. per expert, an exclusive scan over the 16 rows gives each wave's base
 //      inside the expert's group; an exclusive scan over experts gives the
 //      group offsets;
-//   3. each wave walks its segment 64 pairs at a time; lanes holding the same
+//   3. each wave walks its piece 64 pairs at a time; lanes holding the same
 //      expert find each other with one ballot per id bit, rank themselves by
 //      lane order (so the order inside a group is the pair order), and the
 //      highest of them advances the wave's counter for that expert.
-// It also writes the processing order of the groups for the GEMM (non-empty
-// groups, largest first, ties by id) so that the GEMM grid needs no host
-// synchronisation.  Extra workgroups compute the per-row staging shifts of the
-// bf16 activations and clear the row-max buffer of the hidden activations.
+// Up to 8191 pairs one workgroup takes them all.  Beyond, several workgroups
+// take consecutive ranges (three launches: counts per workgroup and expert; a
+// scan over the workgroups; ranks), so the rows of a group still come in pair
+// order.  The group offsets also give the processing order of the groups for
+// the GEMM (non-empty groups, largest first, ties by id), so that the GEMM
+// grid needs no host synchronisation.  Extra workgroups compute the per-row
+// staging shifts of the bf16 activations and clear the row-max buffer of the
+// hidden activations.
+#include <algorithm>
+
 #include "device_util.h"
 
 namespace nvfp4 {
@@ -28,6 +33,10 @@ namespace nvfp4 {
 namespace {
 constexpr int kPermWaves = 16;
 constexpr int kMaxExperts = 512;
+// pair counts from which the permutation runs on several workgroups, and
+// their largest number (each takes whole steps of 1024 pairs)
+constexpr int kPermMultiMin = 8192;
+constexpr int kPermMaxBlocks = 64;
 }  // namespace
 
 // One wave per row: max |x| of the bf16 row, the power-of-two shift that maps
@@ -117,65 +126,67 @@ __device__ void rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift
   }
 }
 
-__global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
-  if (blockIdx.x > 0) {
-    // row shifts of x and clearing of the row-max buffer
-    const int nwav = (gridDim.x - 1) * (blockDim.x / 64);
-    const int w = (blockIdx.x - 1) * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (a.x) rows_to_f16(a.x, a.T, a.H, a.rowshift, a.x16, w, nwav);
-    if (a.zero_buf)
-      for (int i = (blockIdx.x - 1) * blockDim.x + threadIdx.x; i < a.n_zero; i += (gridDim.x - 1) * blockDim.x)
-        a.zero_buf[i] = 0u;
-    return;
-  }
+namespace {
 
-  __shared__ int hist[kPermWaves][kMaxExperts];
-  __shared__ int goff[kMaxExperts + 2];
-  __shared__ __attribute__((aligned(16))) int gsize[kMaxExperts + 4];   // rows of each group (phase 4)
+// LDS of one permutation workgroup (16 waves).
+struct PermLds {
+  int hist[kPermWaves][kMaxExperts];  // per wave: id counts, then the wave's base inside each expert
+  int base[kMaxExperts + 2];          // per expert: first sorted row of this workgroup's pairs / group offsets
+  int gsize[kMaxExperts + 4];         // rows of each group (group order)
+};
 
+// Phase 1: wave w of the workgroup counts the ids of its contiguous piece of
+// the pairs [b0, b1) into hist[w] (LDS atomics: order-free, exact).  The
+// piece is a multiple of 64 pairs; ids are read kBatch steps at a time, so
+// the global load latency is paid once per batch.
+__device__ void count_ids(const int32_t* ids, int E, int b0, int b1, PermLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, P = a.T * a.topk;
-  const int seg = ((P + kPermWaves - 1) / kPermWaves + 63) & ~63;
-  const int f0 = wave * seg, f1 = min(P, f0 + seg);
-
-  for (int i = tid; i < kPermWaves * E; i += blockDim.x) hist[i / E][i % E] = 0;
+  for (int i = tid; i < kPermWaves * E; i += blockDim.x) L.hist[i / E][i % E] = 0;
   __syncthreads();
-
-  // 1. per-wave histograms (ids read kBatch iterations at a time, so the
-  // global load latency is paid once per batch)
+  const int seg = ((b1 - b0 + kPermWaves - 1) / kPermWaves + 63) & ~63;
+  const int f0 = b0 + wave * seg, f1 = min(b1, f0 + seg);
   constexpr int kBatch = 8;
   for (int fb = f0; fb < f1; fb += 64 * kBatch) {
     int idv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int f = fb + 64 * u + lane;
-      idv[u] = f < f1 ? a.ids[f] : -1;
+      idv[u] = f < f1 ? ids[f] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
-      if (idv[u] >= 0 && idv[u] < E) atomicAdd(&hist[wave][idv[u]], 1);
+      if (idv[u] >= 0 && idv[u] < E) atomicAdd(&L.hist[wave][idv[u]], 1);
   }
   __syncthreads();
+}
 
-  // 2a. per expert: exclusive scan over waves, totals into goff[e+1]
-  for (int e = tid; e < E; e += blockDim.x) {
+// Phase 2a: per expert, exclusive scan of the counts over the waves (wave
+// order = pair order); returns nothing, the totals go to tot[e] if tot.
+__device__ void scan_waves(int E, PermLds& L, int* tot) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
 #pragma unroll
     for (int w = 0; w < kPermWaves; ++w) {
-      const int c = hist[w][e];
-      hist[w][e] = run;
+      const int c = L.hist[w][e];
+      L.hist[w][e] = run;
       run += c;
     }
-    goff[e + 1] = run;
+    if (tot) tot[e] = run;
   }
   __syncthreads();
-  // 2b. exclusive scan of the totals (wave 0: each lane sums a contiguous piece)
+}
+
+// Phase 2b: L.base[e + 1] holds group e's row count on entry; on exit L.base
+// holds the exclusive prefix (group offsets), base[E] = routed rows and
+// base[E + 1] = base[E] + the shared group's T rows.  Wave 0: each lane sums
+// a contiguous piece of experts, then a shuffle scan of the lane sums.
+__device__ void scan_experts(int E, int shared_rows, PermLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     const int per = (E + 63) / 64;
     const int e0 = lane * per, e1 = min(E, e0 + per);
     int s = 0;
-    for (int e = e0; e < e1; ++e) s += goff[e + 1];
-    // inclusive scan of lane sums
+    for (int e = e0; e < e1; ++e) s += L.base[e + 1];
     int incl = s;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -184,31 +195,43 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
     }
     int run = incl - s;
     for (int e = e0; e < e1; ++e) {
-      const int c = goff[e + 1];
-      goff[e] = run;
+      const int c = L.base[e + 1];
+      L.base[e] = run;
       run += c;
     }
     if (lane == 63) {
-      goff[E] = incl;                       // rows of valid routed pairs
-      goff[E + 1] = incl + (a.shared ? a.T : 0);
+      L.base[E] = incl;
+      L.base[E + 1] = incl + shared_rows;
     }
   }
   __syncthreads();
+}
 
-  // 3. stable ranks (ids again read kBatch iterations at a time)
+// Phase 3: stable ranks.  Wave w walks its piece of [b0, b1) 64 pairs at a
+// time; lanes holding the same expert find each other with one ballot per id
+// bit and rank themselves by lane order, so the order inside a group is the
+// pair order: row = L.base[id] + L.hist[w][id] + rank; the highest of those
+// lanes advances the wave's count.  Pairs with an id outside [0, E) get
+// inv = -1 and no row.
+__device__ void rank_pairs(const PermuteArgs& a, int b0, int b1, PermLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E = a.E;
+  const int seg = ((b1 - b0 + kPermWaves - 1) / kPermWaves + 63) & ~63;
+  const int f0 = b0 + wave * seg, f1 = min(b1, f0 + seg);
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
+  constexpr int kBatch = 8;
   int idv[kBatch];
-  for (int base = f0; base < f1; base += 64) {
-    const int u = ((base - f0) >> 6) % kBatch;   // wave-uniform
+  for (int fb = f0; fb < f1; fb += 64) {
+    const int u = ((fb - f0) >> 6) % kBatch;   // wave-uniform
     if (u == 0) {
 #pragma unroll
       for (int v = 0; v < kBatch; ++v) {
-        const int fv = base + 64 * v + lane;
+        const int fv = fb + 64 * v + lane;
         idv[v] = fv < f1 ? a.ids[fv] : -1;
       }
     }
-    const int f = base + lane;
+    const int f = fb + lane;
     int id = -1;
 #pragma unroll
     for (int v = 0; v < kBatch; ++v)
@@ -223,20 +246,28 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
     if (id >= 0) {
       const uint64_t below = peers & ((1ull << lane) - 1ull);
       const int rank = __popcll(below);
-      const int pos = goff[id] + hist[wave][id] + rank;
+      const int pos = L.base[id] + L.hist[wave][id] + rank;
       a.perm[pos] = f;
       a.inv[f] = pos;
       if (a.perm_out) a.perm_out[pos] = f;
-      if ((peers >> lane) == 1ull) hist[wave][id] += __popcll(peers);  // highest peer lane
+      if ((peers >> lane) == 1ull) L.hist[wave][id] += __popcll(peers);  // highest peer lane
     } else if (f < f1) {
       a.inv[f] = -1;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
+}
 
-  // shared expert rows
-  const int pv = goff[E];
+// Phase 4, with the group offsets in L.base: the shared expert's rows, the
+// offsets, and the processing order of the groups for the GEMM (non-empty
+// groups, largest first, ties by id), so that the GEMM grid needs no host
+// synchronisation.  Group g's rank counts the groups before it; the sizes are
+// read four at a time (one 16-byte LDS read, the same address in every lane).
+__device__ void finish_groups(const PermuteArgs& a, PermLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int E = a.E, P = a.T * a.topk;
+  const int pv = L.base[E];
   if (a.shared) {
     for (int t = tid; t < a.T; t += blockDim.x) {
       a.perm[pv + t] = P + t;
@@ -245,24 +276,20 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
     }
   }
   for (int i = tid; i < E + 2; i += blockDim.x) {
-    a.offsets[i] = goff[i];
-    if (a.offsets_out) a.offsets_out[i] = goff[i];
+    a.offsets[i] = L.base[i];
+    if (a.offsets_out) a.offsets_out[i] = L.base[i];
   }
-
-  // 4. group order: non-empty groups, largest first, ties by id.  Group g's
-  // rank counts the groups before it; the sizes are read four at a time (one
-  // 16-byte LDS read, the same address in every lane).
   const int G = E + (a.shared ? 1 : 0);
   const int G4 = (G + 3) & ~3;
-  for (int h = tid; h < G4; h += blockDim.x) gsize[h] = h < G ? goff[h + 1] - goff[h] : -1;
+  for (int h = tid; h < G4; h += blockDim.x) L.gsize[h] = h < G ? L.base[h + 1] - L.base[h] : -1;
   __syncthreads();
   for (int g = tid; g < G; g += blockDim.x) {
-    const int mg = gsize[g];
+    const int mg = L.gsize[g];
     if (mg <= 0) continue;
     int rank = 0;
 #pragma unroll 4
     for (int h = 0; h < G4; h += 4) {
-      const int4 m4 = *reinterpret_cast<const int4*>(&gsize[h]);
+      const int4 m4 = *reinterpret_cast<const int4*>(&L.gsize[h]);
       rank += (m4.x > mg) || (m4.x == mg && h < g);
       rank += (m4.y > mg) || (m4.y == mg && h + 1 < g);
       rank += (m4.z > mg) || (m4.z == mg && h + 2 < g);
@@ -273,7 +300,7 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
   if (tid < 64) {
     int cnt = 0, big = 0;
     for (int g = lane; g < G; g += 64) {
-      const int mg = goff[g + 1] - goff[g];
+      const int mg = L.gsize[g];
       cnt += mg > 0;
       big += mg > kBigGroupRows;
     }
@@ -287,6 +314,84 @@ __global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
       a.gcount[1] = big;
     }
   }
+}
+
+// Work of the workgroups after the permutation's own: row shifts and fp16
+// copy of x, clearing of the row-max buffer of the hidden activations.
+__device__ void side_work(const PermuteArgs& a, int first_block) {
+  const int nblk = gridDim.x - first_block, b = blockIdx.x - first_block;
+  const int nwav = nblk * (blockDim.x / 64);
+  const int w = b * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (a.x) rows_to_f16(a.x, a.T, a.H, a.rowshift, a.x16, w, nwav);
+  if (a.zero_buf)
+    for (int i = b * blockDim.x + threadIdx.x; i < a.n_zero; i += nblk * blockDim.x) a.zero_buf[i] = 0u;
+}
+
+}  // namespace
+
+// One workgroup does the whole permutation (pair counts below
+// kPermMultiMin); workgroups 1.. do the side work.
+__global__ __launch_bounds__(1024) void nvfp4_moe_permute(const PermuteArgs a) {
+  if (blockIdx.x > 0) {
+    side_work(a, 1);
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) PermLds L;
+  const int E = a.E, P = a.T * a.topk;
+  count_ids(a.ids, E, 0, P, L);
+  scan_waves(E, L, &L.base[1]);
+  scan_experts(E, a.shared ? a.T : 0, L);
+  rank_pairs(a, 0, P, L);
+  finish_groups(a, L);
+}
+
+// Larger pair counts: nb workgroups, workgroup b taking the pairs
+// [b * seg, (b + 1) * seg), in three launches.
+// 1. per workgroup and expert, the number of pairs: bcnt[b * E + e]
+//    (workgroups nb.. do the side work);
+__global__ __launch_bounds__(1024) void nvfp4_perm_count(const PermuteArgs a, int nb, int seg, int* bcnt) {
+  if ((int)blockIdx.x >= nb) {
+    side_work(a, nb);
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) PermLds L;
+  const int E = a.E, P = a.T * a.topk;
+  const int b0 = blockIdx.x * seg, b1 = max(b0, min(P, b0 + seg));
+  count_ids(a.ids, E, b0, b1, L);
+  scan_waves(E, L, bcnt + (int64_t)blockIdx.x * E);
+}
+
+// 2. one workgroup: per expert, exclusive scan over the workgroups (in place:
+//    bcnt[b * E + e] becomes workgroup b's first row inside group e), group
+//    offsets, shared rows and group order;
+__global__ __launch_bounds__(1024) void nvfp4_perm_scan(const PermuteArgs a, int nb, int* bcnt) {
+  __shared__ __attribute__((aligned(16))) PermLds L;
+  const int E = a.E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = bcnt[(int64_t)b * E + e];
+      bcnt[(int64_t)b * E + e] = run;
+      run += c;
+    }
+    L.base[e + 1] = run;
+  }
+  __syncthreads();
+  scan_experts(E, a.shared ? a.T : 0, L);
+  finish_groups(a, L);
+}
+
+// 3. per workgroup: the counts again, scanned over its waves; ranks from the
+//    group offset + the workgroup's first row in the group.
+__global__ __launch_bounds__(1024) void nvfp4_perm_rank(const PermuteArgs a, int seg, const int* bcnt) {
+  __shared__ __attribute__((aligned(16))) PermLds L;
+  const int E = a.E, P = a.T * a.topk;
+  const int b0 = blockIdx.x * seg, b1 = max(b0, min(P, b0 + seg));
+  count_ids(a.ids, E, b0, b1, L);
+  scan_waves(E, L, nullptr);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) L.base[e] = a.offsets[e] + bcnt[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  rank_pairs(a, b0, b1, L);
 }
 
 __global__ __launch_bounds__(256) void nvfp4_rows_to_f16(const uint16_t* x, int rows, int cols, int* rowshift,
@@ -336,7 +441,12 @@ __global__ __launch_bounds__(1024) void nvfp4_amax_to_gs(const unsigned* rowmax,
   }
 }
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+int permute_blocks(int64_t P) {
+  if (P < kPermMultiMin) return 0;
+  return (int)std::min<int64_t>(kPermMaxBlocks, (P + kPermMultiMin / 8 - 1) / (kPermMultiMin / 8));
+}
+
+hipError_t launch_permute(const PermuteArgs& a, int* bcnt, hipStream_t s) {
   if (a.E > kMaxExperts) return hipErrorInvalidValue;
   int extra = 0;
   if (a.x || a.zero_buf) {
@@ -344,7 +454,18 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
     const int by_zero = a.zero_buf ? (a.n_zero + 1023) / 1024 : 0;
     extra = max(1, min(1024, max(by_rows, by_zero)));
   }
-  hipLaunchKernelGGL(nvfp4_moe_permute, dim3(1 + extra), dim3(1024), 0, s, a);
+  const int P = a.T * a.topk;
+  const int nb = permute_blocks(P);
+  if (nb == 0) {
+    hipLaunchKernelGGL(nvfp4_moe_permute, dim3(1 + extra), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
+  if (!bcnt) return hipErrorInvalidValue;
+  // pieces of whole 1024-pair steps (64 pairs per wave)
+  const int seg = ((P + nb - 1) / nb + 1023) & ~1023;
+  hipLaunchKernelGGL(nvfp4_perm_count, dim3(nb + extra), dim3(1024), 0, s, a, nb, seg, bcnt);
+  hipLaunchKernelGGL(nvfp4_perm_scan, dim3(1), dim3(1024), 0, s, a, nb, bcnt);
+  hipLaunchKernelGGL(nvfp4_perm_rank, dim3(nb), dim3(1024), 0, s, a, seg, static_cast<const int*>(bcnt));
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ def _oracle(x_rows, ids, w, host, shared_host, tokens, a2_gs=None):
     (64, 256, 512, 8, 2, "zipf", False),
     (1, 256, 256, 4, 4, "uniform", True),
     (300, 256, 256, 6, 3, "zipf", True),     # hot groups with > 128 rows: several passes
+    (24, 256, 256, 16, 10, "uniform", True),  # top-10: the combine's loop for more than 8 pairs
 ])
 def test_moe_small_bf16(t, h, i, e, k, routing, shared):
     say(f"moe bf16 T={t} H={h} I={i} E={e} k={k} {routing} shared={shared}")
@@ -160,6 +161,44 @@ def test_moe_fully_fp4_large_batch_with_tiny_groups():
     _check_perm(mi.topk_ids, e, False, off, perm)
     ref = _oracle(xa, mi.topk_ids, mi.topk_w, mi.experts, None, None, a2_gs=a2)
     compare(y, ref, what="fully fp4, tiny groups")
+
+
+def test_moe_permutation_on_several_workgroups():
+    """8800 pairs (more than 8191): the permutation runs on nine workgroups of
+    consecutive 1024-pair ranges, the last one ragged; offsets and sorted-row
+    order stay bit-exact, and so do they with ids out of range (those pairs
+    take no row and contribute nothing)."""
+    t, h, i, e, k = 1100, 256, 256, 64, 8
+    say("moe permutation on several workgroups")
+    mi = synth.make_moe(t, h, i, e, k, seed=21, routing="zipf", shared=True, threads=4)
+    de, ds = DeviceExperts(mi.experts), DeviceExperts(mi.shared)
+    y, off, perm = _run(de, mi.topk_ids, mi.topk_w, x=dev(mi.x), shared=ds)
+    _check_perm(mi.topk_ids, e, True, off, perm)
+    x64 = synth.bf16_to_float64(mi.x)
+    ref = _oracle(x64, mi.topk_ids, mi.topk_w, mi.experts, mi.shared, None)
+    compare(y, ref, what="several permutation workgroups")
+    # ids out of range: the valid pairs keep their stable order, the others go nowhere
+    ids = mi.topk_ids.copy()
+    bad = [(5, 3), (777, 0), (1099, 7), (1024, 2)]
+    for (tt, j), v in zip(bad, (e + 1, -2, 10 ** 6, e)):
+        ids[tt, j] = v
+    y2, off2, perm2 = _run(de, ids, mi.topk_w, x=dev(mi.x), shared=ds)
+    flat = ids.ravel().astype(np.int64)
+    valid = (flat >= 0) & (flat < e)
+    order = np.argsort(np.where(valid, flat, e), kind="stable")[:valid.sum()]
+    exp_off = np.zeros(e + 2, np.int64)
+    exp_off[1:e + 1] = np.cumsum(np.bincount(flat[valid], minlength=e))
+    exp_off[e + 1] = exp_off[e] + t
+    assert np.array_equal(off2, exp_off), "offsets with invalid ids"
+    assert np.array_equal(perm2[:valid.sum()], order), "sorted-row order with invalid ids"
+    assert np.array_equal(perm2[valid.sum():valid.sum() + t], t * k + np.arange(t)), "shared rows"
+    w = mi.topk_w.copy()
+    ids_ok = ids.copy()
+    for tt, j in bad:
+        w[tt, j] = 0
+        ids_ok[tt, j] = 0
+    ref2 = _oracle(x64, ids_ok, w, mi.experts, mi.shared, None)
+    compare(y2, ref2, what="several permutation workgroups, invalid ids")
 
 
 # ---------------------------------------------------------------------------
