@@ -212,7 +212,7 @@ def moe_accounting(cfg, st):
         launches[name] = dict(groups=int(sel.sum()), rows=int(m.sum()),
                               bytes=int(sel.sum()) * BYTES_PER_EXPERT_W1 + int(m.sum()) * row_bytes,
                               flops=int(m.sum()) * 2 * (2 * i * h))
-    return dict(touched=touched, flops=flops, step_bytes=step_bytes, g1=launches)
+    return dict(touched=touched, flops=flops, step_bytes=step_bytes, g1=launches, large_batch=large_batch)
 
 
 def moe_cpu_baseline(cfg, st, budget_s=12.0):
@@ -307,7 +307,8 @@ def run_moe(args, cfg):
     src = kernel_source_hash()
     gbs = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
     tflops = acc["flops"] / (ms_step * 1e-3) / 1e12
-    kern = {"big": "nvfp4_gemm_lds (gate/up + SwiGLU, groups of > 4 rows)",
+    kern = {"big": "nvfp4_gemm_lds (gate/up + SwiGLU, " +
+                   ("all groups: > 16 rows per group on average)" if acc["large_batch"] else "groups of > 4 rows)"),
             "small": "nvfp4_gemm_compact (gate/up + SwiGLU, groups of <= 4 rows)"}[part]
     if cfg["fp4"]:
         kern = kern.replace("nvfp4_gemm_compact", "nvfp4_gemm_direct")
@@ -398,6 +399,26 @@ def run_linear(args, cfg):
     nbytes = w_bytes + m * k * 2 + m * n * 2
     flops = 2 * m * n * k
     gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import linear
+        log("timing the CPU oracle on a bounded sample ...")
+        ms_rows = min(m, 8)
+        xs = synth.bf16_to_float64(li.x[:ms_rows])
+        t_start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t_start < 10.0:
+            linear.linear_bf16(xs, li.w, li.w_sf, li.ws2)
+            reps += 1
+        sec = (time.perf_counter() - t_start) / reps
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        sample_bytes = w_bytes + ms_rows * k * 2 + ms_rows * n * 2
+        cpu = dict(value=round(sample_bytes / sec / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                   sample=f"{ms_rows} token row{'s' if ms_rows > 1 else ''} against the whole weight, float64 numpy oracle, {reps} "
+                          f"repetitions in about 10 s; dequantization runs on one thread, the product on the "
+                          f"BLAS pool")
     return {
         "metric": "NVFP4 linear HBM GB/s (%roofline), 1xMI355X", "value": round(gbs, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -407,7 +428,7 @@ def run_linear(args, cfg):
         "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None),
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
 
 
