@@ -200,7 +200,9 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
  *   [0] permute [1] gate/up GEMM, groups of > 4 rows [2] gate/up GEMM, the
  *   other groups [3] calibration and conversion of h (fp32 h only) [4] down
  *   GEMM, groups of > 4 rows [5] down GEMM, the other groups [6] combine
- *   [7] end; event i is recorded before the work it names, so stage i lasts
+ *   [7] end (when the groups average more than 16 rows, [1] and [4] cover
+ *   every group and [2] and [5] are empty); event i is recorded before the
+ *   work it names, so stage i lasts
  *   from event i to event i + 1.  NULL entries are skipped (each recorded
  *   event costs a few microseconds between two kernels).
  */
