@@ -26,9 +26,36 @@ int pick_maxc(double rows_per_group) {
   return 8;
 }
 
+// K splits of a MoE GEMM's groups of more than 4 rows (four-wave LDS kernel)
+// at decode-sized batches (at most 2 rows per group on average): there those
+// groups are few and each work item is a chain of dependent K chunks, so a K
+// range of at least 16 chunks is split 4 or 2 ways (at least 4 chunks per
+// split; the gate/up GEMM at hidden 7168: 4 x 7).  Shorter ranges are not
+// split (measured on MI355X at decode: the down GEMM's 8 chunks split 2 ways
+// gained nothing, 4 ways lost 17 us).
+int moe_splits(int64_t T, int64_t topk, int64_t E, int64_t S, int64_t K) {
+  if ((double)(T * topk + S * T) / (double)(E + S) > 2.0) return 1;
+  const int64_t nkc = K / 256;
+  if (nkc < 16) return 1;
+  for (int s : {4, 2})
+    if (nkc % s == 0 && nkc / s >= 4) return s;
+  return 1;
+}
+
+// Groups of more than 4 rows: at most this many (the big-group launch's list part).
+int64_t moe_big_groups(int64_t T, int64_t topk, int64_t E, int64_t S) {
+  return std::min<int64_t>(E + S, (T * topk + S * T) / (kBigGroupRows + 1));
+}
+
+// Rows per pass of the four-wave LDS kernel at decode/prefill (GemmShape{4, 2, 4}).
+constexpr int kMoeSmallPassRows = 64;
+
 // Workspace layout of nvfp4_moe_grouped.
 struct MoeLayout {
-  size_t offsets, glist, gcount, perm, inv, bcnt, rowshift, x16, hmax, hshift, h, h16, hq, hq_sf, slot, total;
+  size_t offsets, glist, gcount, perm, inv, bcnt, rowshift, x16, hmax, hshift, h, h16, hq, hq_sf, slot, mpart, mcnt,
+      total;
+  int s1, s2;        // K splits of the gate/up and down GEMMs
+  int mpass, nbmax;  // split counters: G * nbmax * mpass
 };
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared, int h_fp4) {
@@ -57,6 +84,19 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, i
     L.hq = L.hq_sf = 0;
   }
   L.slot = take(sizeof(uint16_t) * (size_t)Pt * H);
+  L.s1 = moe_splits(T, topk, E, S, H);
+  L.s2 = moe_splits(T, topk, E, S, I);
+  // the partial sums are addressed with 32-bit offsets
+  if ((int64_t)sizeof(float) * Pt * std::max<int64_t>(L.s1 * 2 * I, L.s2 * H) >= kMaxBuffer) L.s1 = L.s2 = 1;
+  // a group holds at most max(T * topk, T) rows (ids need not be distinct)
+  L.mpass = (int)((std::max(T * topk, T) + kMoeSmallPassRows - 1) / kMoeSmallPassRows);
+  L.nbmax = (int)std::max(L.s1 > 1 ? I / gemm_rows_per_block(EPI_SWIGLU_F32, GemmShape{4, 2, 4}) : 0,
+                          L.s2 > 1 ? H / gemm_rows_per_block(EPI_SLOT, GemmShape{4, 2, 4}) : 0);
+  L.mpart = L.mcnt = 0;
+  if (L.s1 > 1 || L.s2 > 1) {
+    L.mpart = take(sizeof(float) * (size_t)Pt * std::max<int64_t>(L.s1 * 2 * I, L.s2 * H));
+    L.mcnt = take(sizeof(uint32_t) * (size_t)moe_big_groups(T, topk, E, S) * L.nbmax * L.mpass);
+  }
   L.total = off;
   return L;
 }
@@ -358,13 +398,13 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   };
   // Groups with more than kBigGroupRows rows run on the LDS-staged kernel; at
   // most Pt / (kBigGroupRows + 1) groups can be that big.
-  const int n_big_max = std::min(G, Pt / (kBigGroupRows + 1));
+  const int n_big_max = (int)moe_big_groups(T, k, E, S);
   const double rows_per_group = (double)Pt / (double)G;
   // big groups: 64-row passes on 4-wave workgroups (a few hot groups), or
   // 112-row passes on 8-wave workgroups sharing one LDS tile (large batches)
   const bool large_batch = rows_per_group > 16;
   // ev_big / ev_small: stage events recorded before each of the two launches
-  auto two_launches = [&](GemmArgs g, int amode, int epi, int r, int ev_big, int ev_small) -> bool {
+  auto two_launches = [&](GemmArgs g, int amode, int epi, int r, int ev_big, int ev_small, int msplit) -> bool {
     // (the 8-wave configuration walks K in quads of 256-element chunks)
     GemmShape big = !large_batch ? GemmShape{4, r, 4} : g.K % 1024 == 0 ? GemmShape{7, 4, 8} : GemmShape{8, r, 4};
     GemmShape small{1, r, 4};
@@ -381,7 +421,17 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
     }
     g.list_part = 0;
     g.nb = (int)((g.N / half + gemm_rows_per_block(epi, big) - 1) / gemm_rows_per_block(epi, big));
-    if (launch_gemm(g, amode, epi, big, n_big_max, s) != hipSuccess) return false;
+    g.mks = 1;
+    if (msplit > 1) {
+      g.mks = msplit;
+      g.mpart = reinterpret_cast<float*>(ws + L.mpart);
+      g.mrows = Pt;
+      g.mcols = g.N;
+      g.mpass = L.mpass;
+      g.mcnt = reinterpret_cast<unsigned*>(ws + L.mcnt);
+    }
+    if (launch_gemm(g, amode, epi, big, n_big_max * g.mks, s) != hipSuccess) return false;
+    g.mks = 1;
     ev(ev_small);
     g.list_part = 1;
     g.nb = (int)((g.N / half + gemm_rows_per_block(epi, small) - 1) / gemm_rows_per_block(epi, small));
@@ -409,6 +459,10 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   pa.x16 = x16;
   pa.zero_buf = h_fp4 ? nullptr : hmax;
   pa.n_zero = Pt;
+  if (L.mcnt) {
+    pa.zero_buf2 = reinterpret_cast<unsigned*>(ws + L.mcnt);
+    pa.n_zero2 = (int)(moe_big_groups(T, k, E, S) * L.nbmax * L.mpass);
+  }
   if (launch_permute(pa, reinterpret_cast<int*>(ws + L.bcnt), s) != hipSuccess) return NVFP4_ERR_LAUNCH;
 
   // 2. gate/up GEMM with fused SwiGLU
@@ -443,7 +497,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g1.hq_sf = h_fp4 ? ws + L.hq_sf : nullptr;
   g1.h_gs = a->a2_gs;
   const int epi1 = h_fp4 ? EPI_SWIGLU_FP4 : EPI_SWIGLU_F32;
-  if (!two_launches(g1, fp4 ? A_FP4 : A_F16, epi1, 2, 1, 2)) return NVFP4_ERR_LAUNCH;
+  if (!two_launches(g1, fp4 ? A_FP4 : A_F16, epi1, 2, 1, 2, L.s1)) return NVFP4_ERR_LAUNCH;
 
   // 3. calibration and fp16 copy of h (unless it is NVFP4), down GEMM scattering each pair's row
   ev(3);
@@ -480,7 +534,7 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   g2.rowshift = hshift;
   g2.gsa = h_fp4 ? a->a2_gs : nullptr;
   g2.slot = slot;
-  if (!two_launches(g2, h_fp4 ? A_FP4 : A_F16, EPI_SLOT, 2, 4, 5)) return NVFP4_ERR_LAUNCH;
+  if (!two_launches(g2, h_fp4 ? A_FP4 : A_F16, EPI_SLOT, 2, 4, 5, L.s2)) return NVFP4_ERR_LAUNCH;
 
   // 4. weighted combine
   ev(6);

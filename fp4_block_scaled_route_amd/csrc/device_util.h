@@ -23,6 +23,18 @@ __device__ __forceinline__ u32x4 buf_load16_nt(rsrc_t r, uint32_t voff, uint32_t
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// 16-byte load and store that bypass the L1 and L2 caches (cache policy sc0
+// sc1: system coherent): data one workgroup hands to another on a different
+// XCD within a launch, without a device-wide fence (which writes back and
+// invalidates the whole L2).
+constexpr int kCoherent = 1 | 16;
+__device__ __forceinline__ u32x4 buf_load16_coherent(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCoherent));
+}
+__device__ __forceinline__ void buf_store16_coherent(u32x4 v, rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                         voff, 0, kCoherent);
+}
 
 // 8 E2M1 codes (element e in nibble e of `w`) times one E4M3 block scale,
 // as 8 fp16.  Exact: |E2M1 * E4M3| lies in {0} U [2^-10, 2688] and needs at

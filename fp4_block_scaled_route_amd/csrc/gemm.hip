@@ -83,6 +83,7 @@ constexpr int kVmcnt0 = 0x0F70;
 // Resolved work item.
 struct Item {
   int g, row0, m;
+  int gl;              // MoE: position in this launch's part of the group list
   int ks;              // K split (grouped linear), else 0
   const uint8_t* W;
   const uint8_t* WS;
@@ -92,8 +93,14 @@ struct Item {
 __device__ __forceinline__ bool resolve_item(const GemmArgs& a, int gi, Item& it) {
   it.ks = 0;
   if (a.offsets) {
+    if (a.mks > 1) {
+      const int gi2 = gi / a.mks;
+      it.ks = gi - gi2 * a.mks;
+      gi = gi2;
+    }
     const int lo = a.list_part == 1 ? a.gcount[1] : 0;
     const int hi = a.list_part == 0 ? a.gcount[1] : a.gcount[0];
+    it.gl = gi;
     gi += lo;
     if (gi >= hi) return false;
     it.g = a.glist[gi];
@@ -689,7 +696,7 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
   // chunks of this item: [kbase, kbase + nkc) (all of K unless K is split)
-  const int nkc = K / kChunk / (a.ksplit > 1 ? a.ksplit : 1);
+  const int nkc = K / kChunk / (a.ksplit > 1 ? a.ksplit : a.mks > 1 ? a.mks : 1);
   const int kbase = it.ks * nkc;
   const int last = nkc - 1;
   const int seg = AM == A_F16 ? lane & 31 : lg;
@@ -915,6 +922,60 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         __syncthreads();
       }
       if (kc < nkc) compute(0, wb, last, 0);
+    }
+    if constexpr (NW == kNW) {
+      if (a.mks > 1) {
+        // K split of a MoE item: this split's sums go to mpart; the split
+        // that counts itself last adds all of them in split order and runs
+        // the epilogue (no split waits for another).  The sums are written
+        // and read past the caches and complete (vmcnt(0)) before the count,
+        // which is a device-scope atomic.
+        __shared__ int s_last;
+        const rsrc_t rp = make_rsrc(a.mpart, (uint32_t)((int64_t)a.mks * a.mrows * a.mcols * 4));
+        auto mcol = [&](int f) {
+          return (is_swiglu<EP>() && (f & 1) ? a.I : 0) + fr.fbase[f] + 4 * lg;
+        };
+        const uint32_t sstride = (uint32_t)a.mrows * a.mcols * 4;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+          const int tr = pbase + 16 * c + lr;
+          if (c >= nc || tr >= pbase + prow) continue;
+          const uint32_t base = (uint32_t)it.ks * sstride + (uint32_t)(it.row0 + tr) * a.mcols * 4;
+#pragma unroll
+          for (int f = 0; f < R; ++f)
+            if (fr.fvalid[f]) buf_store16_coherent(__builtin_bit_cast(u32x4, acc[f][c]), rp, base + mcol(f) * 4);
+        }
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const int tile = (it.gl * a.nb + nbk) * a.mpass + pass;
+          const bool last_split =
+              __hip_atomic_fetch_add(a.mcnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.mks - 1);
+          if (last_split) a.mcnt[tile] = 0u;   // every split has counted: ready for the next launch
+          s_last = last_split;
+        }
+        __syncthreads();
+        if (!s_last) continue;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+          const int tr = pbase + 16 * c + lr;
+          if (c >= nc || tr >= pbase + prow) continue;
+          const uint32_t base = (uint32_t)(it.row0 + tr) * a.mcols * 4;
+#pragma unroll
+          for (int f = 0; f < R; ++f) {
+            if (!fr.fvalid[f]) continue;
+            f32x4 s = __builtin_bit_cast(f32x4, buf_load16_coherent(rp, base + mcol(f) * 4));
+            for (int k = 1; k < a.mks; ++k) {
+              const f32x4 v = __builtin_bit_cast(f32x4, buf_load16_coherent(rp, k * sstride + base + mcol(f) * 4));
+              s[0] += v[0];
+              s[1] += v[1];
+              s[2] += v[2];
+              s[3] += v[3];
+            }
+            acc[f][c] = s;
+          }
+        }
+      }
     }
     epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
   }

@@ -72,6 +72,16 @@ struct GemmArgs {
   // (EPI_PART_F32), added in split order by launch_split_reduce.
   int ksplit;
   float* part;
+  // K split of the MoE groups on the four-wave LDS kernel (mks > 1; decode-
+  // sized batches): item = ((group list index, split), weight-row block); each
+  // split writes its fp32 sums to mpart [mks, rows, mcols] (rows = sorted
+  // rows) and counts itself in mcnt[(list position * nb + block) * mpass + pass]
+  // (zeroed before the launch); the last one adds the mks partial sums in
+  // split order and runs the epilogue, then clears the counter.
+  int mks;
+  float* mpart;
+  int mrows, mcols, mpass;
+  unsigned* mcnt;
   int nb;              // weight-row blocks per group (grid = groups * nb)
   // Activation operand.
   const void* a;       // see AMode; row pitch in elements = K
@@ -123,6 +133,8 @@ struct PermuteArgs {
   f16* x16;            // [T, H]
   unsigned* zero_buf;  // [n_zero] set to 0, or nullptr
   int n_zero;
+  unsigned* zero_buf2; // [n_zero2] set to 0, or nullptr
+  int n_zero2;
 };
 // Workgroups of the multi-workgroup permutation for P pairs (0: one
 // workgroup does it all); it needs bcnt[blocks * E] ints of workspace.

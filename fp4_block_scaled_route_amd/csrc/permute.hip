@@ -317,7 +317,8 @@ __device__ void finish_groups(const PermuteArgs& a, PermLds& L) {
 }
 
 // Work of the workgroups after the permutation's own: row shifts and fp16
-// copy of x, clearing of the row-max buffer of the hidden activations.
+// copy of x, clearing of the row-max buffer of the hidden activations and of
+// the GEMMs' split counters.
 __device__ void side_work(const PermuteArgs& a, int first_block) {
   const int nblk = gridDim.x - first_block, b = blockIdx.x - first_block;
   const int nwav = nblk * (blockDim.x / 64);
@@ -325,6 +326,8 @@ __device__ void side_work(const PermuteArgs& a, int first_block) {
   if (a.x) rows_to_f16(a.x, a.T, a.H, a.rowshift, a.x16, w, nwav);
   if (a.zero_buf)
     for (int i = b * blockDim.x + threadIdx.x; i < a.n_zero; i += nblk * blockDim.x) a.zero_buf[i] = 0u;
+  if (a.zero_buf2)
+    for (int i = b * blockDim.x + threadIdx.x; i < a.n_zero2; i += nblk * blockDim.x) a.zero_buf2[i] = 0u;
 }
 
 }  // namespace
@@ -449,9 +452,10 @@ int permute_blocks(int64_t P) {
 hipError_t launch_permute(const PermuteArgs& a, int* bcnt, hipStream_t s) {
   if (a.E > kMaxExperts) return hipErrorInvalidValue;
   int extra = 0;
-  if (a.x || a.zero_buf) {
+  if (a.x || a.zero_buf || a.zero_buf2) {
     const int by_rows = a.x ? (a.T + 15) / 16 : 0;   // 16 waves per block, one row each
-    const int by_zero = a.zero_buf ? (a.n_zero + 1023) / 1024 : 0;
+    // (clearing takes at most 4 extra workgroups: they loop over the words)
+    const int by_zero = min(4, max(a.zero_buf ? (a.n_zero + 1023) / 1024 : 0, a.zero_buf2 ? (a.n_zero2 + 1023) / 1024 : 0));
     extra = max(1, min(1024, max(by_rows, by_zero)));
   }
   const int P = a.T * a.topk;

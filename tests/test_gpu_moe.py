@@ -201,6 +201,46 @@ def test_moe_permutation_on_several_workgroups():
     compare(y2, ref2, what="several permutation workgroups, invalid ids")
 
 
+@pytest.mark.parametrize("t,h,i,e,k,routing,shared,fp4", [
+    (66, 2048, 256, 100, 2, "uniform", True, False),   # gate/up K split 2 ways; shared group of 66 rows: 2 passes
+    (66, 256, 2048, 100, 2, "uniform", True, False),   # down K split 2 ways
+    (24, 2048, 256, 48, 2, "zipf", False, True),       # fully FP4 (NVFP4 h epilogue) with the gate/up split
+])
+def test_moe_decode_sized_k_split(t, h, i, e, k, routing, shared, fp4):
+    """At most 2 rows per group on average: the groups of more than 4 rows are
+    few, and their K range is split; the last split to finish adds the partial
+    sums in split order, so two calls agree bit for bit."""
+    say(f"moe decode-sized K split T={t} H={h} I={i} E={e} k={k} fp4={fp4}")
+    mi = synth.make_moe(t, h, i, e, k, seed=31, routing=routing, zipf_s=1.6, shared=shared, threads=4)
+    counts = np.bincount(mi.topk_ids.ravel(), minlength=e)
+    assert (t * k + (t if shared else 0)) / (e + (1 if shared else 0)) <= 2.0
+    assert shared or counts.max() > 4
+    de = DeviceExperts(mi.experts)
+    ds = DeviceExperts(mi.shared) if shared else None
+    if fp4:
+        xq, xs, gs = ops.quantize_act(dev(mi.x))
+        rq, rs, rgs = quant.quantize_nvfp4(mi.x.float().numpy())
+        xa = quant.dequantize_nvfp4(rq, rs, rgs)
+        amax = 0.0
+        for tt in range(t):
+            for j in range(k):
+                ex = mi.experts.expert(int(mi.topk_ids[tt, j]))
+                amax = max(amax, moe.hidden_amax(xa[tt:tt + 1], codec.dequant_nvfp4(*ex[:3])))
+        a2 = np.float32(np.float32(amax) / np.float32(2688.0))
+        kw = dict(x_fp4=xq, x_sf=xs, a1_gs=gs, a2_gs=f32(a2))
+        x_ref = xa
+    else:
+        a2 = None
+        kw = dict(x=dev(mi.x))
+        x_ref = synth.bf16_to_float64(mi.x)
+    y, off, perm = _run(de, mi.topk_ids, mi.topk_w, shared=ds, **kw)
+    y2, _, _ = _run(de, mi.topk_ids, mi.topk_w, shared=ds, **kw)
+    assert torch.equal(y, y2), "K-split sums differ between calls"
+    _check_perm(mi.topk_ids, e, shared, off, perm)
+    ref = _oracle(x_ref, mi.topk_ids, mi.topk_w, mi.experts, mi.shared if shared else None, None, a2_gs=a2)
+    compare(y, ref, what="decode-sized K split")
+
+
 # ---------------------------------------------------------------------------
 # full DeepSeek-V4-shaped configurations, sampled tokens
 # ---------------------------------------------------------------------------
