@@ -202,15 +202,17 @@ def test_moe_permutation_on_several_workgroups():
 
 
 @pytest.mark.parametrize("t,h,i,e,k,routing,shared,fp4", [
-    (66, 2048, 256, 100, 2, "uniform", True, False),   # gate/up K split 2 ways; shared group of 66 rows: 2 passes
-    (66, 256, 2048, 100, 2, "uniform", True, False),   # down K split 2 ways
-    (24, 2048, 256, 48, 2, "zipf", False, True),       # fully FP4 (NVFP4 h epilogue) with the gate/up split
+    (66, 4096, 256, 100, 2, "uniform", True, False),   # shared group of 66 rows: 2 passes, each split
+    (40, 4096, 512, 64, 2, "zipf", True, False),       # hot routed groups next to the shared one
+    (24, 4096, 256, 48, 2, "zipf", False, True),       # fully FP4 (NVFP4 h epilogue)
 ])
 def test_moe_decode_sized_k_split(t, h, i, e, k, routing, shared, fp4):
-    """At most 2 rows per group on average: the groups of more than 4 rows are
-    few, and their K range is split; the last split to finish adds the partial
-    sums in split order, so two calls agree bit for bit."""
+    """At most 2 rows per group on average and a gate/up K range of at least
+    16 chunks: the K range of the groups of more than 4 rows is split 4 ways;
+    the last split to finish adds the partial sums in split order, so two calls
+    agree bit for bit."""
     say(f"moe decode-sized K split T={t} H={h} I={i} E={e} k={k} fp4={fp4}")
+    assert h // 256 >= 16
     mi = synth.make_moe(t, h, i, e, k, seed=31, routing=routing, zipf_s=1.6, shared=shared, threads=4)
     counts = np.bincount(mi.topk_ids.ravel(), minlength=e)
     assert (t * k + (t if shared else 0)) / (e + (1 if shared else 0)) <= 2.0
