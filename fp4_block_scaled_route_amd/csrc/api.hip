@@ -435,6 +435,9 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
     ev(ev_small);
     g.list_part = 1;
     g.nb = (int)((g.N / half + gemm_rows_per_block(epi, small) - 1) / gemm_rows_per_block(epi, small));
+    // more than 2 rows per group on average: a group's workgroups on one XCD
+    // (measured on MI355X: prefill 1.3-1.6% faster; decode 0.5% slower)
+    g.xcd_order = rows_per_group > 2.0;
     return launch_gemm(g, amode, epi, small, G, s) == hipSuccess;
   };
 

@@ -417,8 +417,18 @@ void nvfp4_gemm_compact(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   Item it;
-  if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
-  const int nbk = blockIdx.x % a.nb;
+  int gi0, nbk;
+  if (a.xcd_order) {
+    // workgroup b runs on XCD b % 8; XCD x takes groups x, x + 8, ... with
+    // all nb row blocks of a group in a row, so one L2 holds its activations
+    const int j = blockIdx.x >> 3;
+    gi0 = (j / a.nb) * 8 + (blockIdx.x & 7);
+    nbk = j % a.nb;
+  } else {
+    gi0 = blockIdx.x / a.nb;
+    nbk = blockIdx.x % a.nb;
+  }
+  if (!resolve_item(a, gi0, it)) return;
   Frags<R, EP> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
@@ -538,8 +548,18 @@ void nvfp4_gemm_direct(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   Item it;
-  if (!resolve_item(a, blockIdx.x / a.nb, it)) return;
-  const int nbk = blockIdx.x % a.nb;
+  int gi0, nbk;
+  if (a.xcd_order) {
+    // workgroup b runs on XCD b % 8; XCD x takes groups x, x + 8, ... with
+    // all nb row blocks of a group in a row, so one L2 holds its activations
+    const int j = blockIdx.x >> 3;
+    gi0 = (j / a.nb) * 8 + (blockIdx.x & 7);
+    nbk = j % a.nb;
+  } else {
+    gi0 = blockIdx.x / a.nb;
+    nbk = blockIdx.x % a.nb;
+  }
+  if (!resolve_item(a, gi0, it)) return;
   Frags<R, EP> fr;
   fr.init(a, it, nbk, wave, lr, lg);
   const int K = a.K;
@@ -990,6 +1010,7 @@ namespace {
 template <int AM, int EP, int R>
 hipError_t launch_direct(const GemmArgs& a, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
+  if (a.xcd_order) n_items = (n_items / a.nb + 7) / 8 * 8 * a.nb;   // whole rounds of 8 groups
   if constexpr (AM == A_F16)
     hipLaunchKernelGGL((nvfp4_gemm_compact<R, EP>), dim3(n_items), dim3(kNW * 64), 0, s, a);
   else

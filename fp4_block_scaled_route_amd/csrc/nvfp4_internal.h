@@ -78,6 +78,8 @@ struct GemmArgs {
   // rows) and counts itself in mcnt[(list position * nb + block) * mpass + pass]
   // (zeroed before the launch); the last one adds the mks partial sums in
   // split order and runs the epilogue, then clears the counter.
+  // MoE groups on the barrier-free kernels in XCD order (see the kernels)
+  int xcd_order;
   int mks;
   float* mpart;
   int mrows, mcols, mpass;
