@@ -371,11 +371,19 @@ __global__ __launch_bounds__(1024) void nvfp4_perm_scan(const PermuteArgs a, int
   __shared__ __attribute__((aligned(16))) PermLds L;
   const int E = a.E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    // counts requested 16 at a time before their first use (one memory
+    // round trip per 16 workgroups instead of one per workgroup)
+    constexpr int kB = 16;
     int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int c = bcnt[(int64_t)b * E + e];
-      bcnt[(int64_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nb; b0 += kB) {
+      int c[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) c[u] = b0 + u < nb ? bcnt[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (b0 + u < nb) bcnt[(int64_t)(b0 + u) * E + e] = run;
+        run += c[u];
+      }
     }
     L.base[e + 1] = run;
   }
