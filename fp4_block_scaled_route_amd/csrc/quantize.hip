@@ -18,7 +18,7 @@ namespace nvfp4 {
 
 __global__ void nvfp4_quant_zero(float* gs) { gs[0] = 0.0f; }
 
-// Grid-wide max |x|: every thread folds 4 independent 16-byte loads per
+// Grid-wide max |x|: every thread folds 8 independent 16-byte loads per
 // iteration, the block reduces through LDS, and one atomic per block (not per
 // wave: thousands of atomics on one word serialise) merges the blocks.
 __global__ __launch_bounds__(256) void nvfp4_quant_amax(const uint16_t* x, int64_t n8, float* amax_word) {
@@ -34,6 +34,13 @@ __global__ __launch_bounds__(256) void nvfp4_quant_amax(const uint16_t* x, int64
     }
   };
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n8; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = v4[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) fold(v[u]);
+  }
   for (; i + 3 * stride < n8; i += 4 * stride) {
     const uint4 a = v4[i], b = v4[i + stride], c = v4[i + 2 * stride], d = v4[i + 3 * stride];
     fold(a);
