@@ -289,7 +289,10 @@ def run_moe(args, cfg):
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    k_ms = sum(hip.elapsed_ms(e[0], e[1]) for e in kev) / args.steps
+    k_list = sorted(hip.elapsed_ms(e[0], e[1]) for e in kev)
+    k_ms = sum(k_list) / args.steps
+    k_med = k_list[len(k_list) // 2]
+    k_p90 = k_list[min(len(k_list) - 1, int(0.9 * len(k_list)))]
     for e in kev:
         hip.destroy(e)
     names = ["permute", "gate_up_big", "gate_up_small", "h_to_f16", "down_big", "down_small", "combine"]
@@ -322,7 +325,8 @@ def run_moe(args, cfg):
         ach = kb / (k_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic)
-    roof.update(kernel=kern, kernel_ms=round(k_ms, 4), groups=acc["g1"][part]["groups"],
+    roof.update(kernel=kern, kernel_ms=round(k_ms, 4), kernel_ms_median=round(k_med, 4), kernel_ms_p90=round(k_p90, 4),
+                groups=acc["g1"][part]["groups"],
                 algorithmic_bytes_per_launch=kb, algorithmic_flops_per_launch=kf)
     cpu = None
     if not args.no_cpu_baseline:
