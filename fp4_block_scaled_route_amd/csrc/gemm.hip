@@ -79,6 +79,13 @@ constexpr int block_rows() { return is_swiglu<EP>() ? NW * (R / 2) * 16 : NW * R
 constexpr int kNW = 4;  // waves per workgroup
 // s_waitcnt operand (gfx9 encoding) waiting for all vector memory loads only
 constexpr int kVmcnt0 = 0x0F70;
+// Requests for chunks past the end of a work item (the prefetches of its last
+// steps) keep their place in the code, so the pipeline has no branches, but
+// with this bit in their lane offset they fall outside the buffer resource:
+// the hardware returns zeros without touching memory (re-reading the last
+// chunk instead cost 2 of every 8 chunks' traffic on short-K items: the
+// non-temporal code loads go back to HBM).  The results are never used.
+constexpr uint32_t kPast = 0x80000000u;
 
 // Resolved work item.
 struct Item {
@@ -216,7 +223,8 @@ struct Frags {
   // the last chunk), both at once, so the row's 128 scale bytes of the group
   // are requested together; transpose4 of raw[f][h] then gives every lane its
   // word of chunks 8*sc+4h .. 8*sc+4h+3.
-  __device__ __forceinline__ void load_scales8(u32x4 (&raw)[R][2], int sc, int nkc, int lg, int kbase = 0) const {
+  __device__ __forceinline__ void load_scales8(u32x4 (&raw)[R][2], int sc, int nkc, int lg, int kbase = 0,
+                                               uint32_t past = 0) const {
     const int k0 = kbase + min(8 * sc + lg, nkc - 1);
     const int k1 = kbase + min(8 * sc + 4 + lg, nkc - 1);
 #pragma unroll
@@ -224,21 +232,21 @@ struct Frags {
       // (down GEMM: with the non-temporal hint, measured 3% faster on MI355X;
       // gate/up: 8% slower with it)
       if constexpr (EP == EPI_SLOT) {
-        raw[f][0] = buf_load16_nt(rs, vs - lg * 4 + k0 * 16, ss[f]);
-        raw[f][1] = buf_load16_nt(rs, vs - lg * 4 + k1 * 16, ss[f]);
+        raw[f][0] = buf_load16_nt(rs, (vs - lg * 4 + k0 * 16) | past, ss[f]);
+        raw[f][1] = buf_load16_nt(rs, (vs - lg * 4 + k1 * 16) | past, ss[f]);
       } else {
-        raw[f][0] = buf_load16(rs, vs - lg * 4 + k0 * 16, ss[f]);
-        raw[f][1] = buf_load16(rs, vs - lg * 4 + k1 * 16, ss[f]);
+        raw[f][0] = buf_load16(rs, (vs - lg * 4 + k0 * 16) | past, ss[f]);
+        raw[f][1] = buf_load16(rs, (vs - lg * 4 + k1 * 16) | past, ss[f]);
       }
     }
   }
 
-  __device__ __forceinline__ void load(WBuf<R>& wb, int kc) const {
+  __device__ __forceinline__ void load(WBuf<R>& wb, int kc, uint32_t past = 0) const {
 #pragma unroll
     for (int f = 0; f < R; ++f) {
-      wb.c0[f] = buf_load16(rw, vw, sw[f] + kc * 128);
-      wb.c1[f] = buf_load16(rw, vw + 16, sw[f] + kc * 128);
-      wb.s[f] = buf_load4(rs, vs, ss[f] + kc * 16);
+      wb.c0[f] = buf_load16(rw, vw | past, sw[f] + kc * 128);
+      wb.c1[f] = buf_load16(rw, (vw + 16) | past, sw[f] + kc * 128);
+      wb.s[f] = buf_load4(rs, vs | past, ss[f] + kc * 16);
     }
   }
 };
@@ -462,9 +470,15 @@ void nvfp4_gemm_compact(const GemmArgs a) {
     for (int f = 0; f < R; ++f) acc[f][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     u32x4 bq0a, bq0b, bq1a, bq1b;   // compact activation loads, two chunks in flight
+    // kc past the end: no memory access (kPast)
     auto bload = [&](u32x4& x, u32x4& y, int kc) {
-      x = buf_load16(rb, vb0, (kbase + kc) * kChunk * 2);
-      if (two) y = buf_load16(rb, vb1, (kbase + kc) * kChunk * 2);
+      const uint32_t past = kc > last ? kPast : 0u;
+      kc = min(kc, last);
+      x = buf_load16(rb, vb0 | past, (kbase + kc) * kChunk * 2);
+      if (two) y = buf_load16(rb, vb1 | past, (kbase + kc) * kChunk * 2);
+    };
+    auto codes = [&](u32x4 (&h0)[R], u32x4 (&h1)[R], int kc) {
+      fr.load_codes_rows(h0, h1, kc > last ? vrow | kPast : vrow, kbase + min(kc, last));
     };
     auto bstore = [&](uint8_t* slot, const u32x4& x, const u32x4& y) {
       *reinterpret_cast<u32x4*>(slot + wr0) = x;
@@ -496,11 +510,11 @@ void nvfp4_gemm_compact(const GemmArgs a) {
     // prologue
     fr.load_scales8(sraw, 0, nkc, lg, kbase);
     bload(bq0a, bq0b, 0);
-    bload(bq1a, bq1b, min(1, last));
-    fr.load_codes_rows(wc0a, wc1a, vrow, kbase);
-    fr.load_codes_rows(wc0b, wc1b, vrow, kbase + min(1, last));
+    bload(bq1a, bq1b, 1);
+    codes(wc0a, wc1a, 0);
+    codes(wc0b, wc1b, 1);
     bstore(slot0, bq0a, bq0b);
-    bload(bq0a, bq0b, min(2, last));
+    bload(bq0a, bq0b, 2);
 
     // one iteration = one group of 8 chunks; chunk kc uses codes set (kc%2),
     // activation slot (kc%2); at its end the activations of chunk kc+1 are
@@ -514,21 +528,21 @@ void nvfp4_gemm_compact(const GemmArgs a) {
           transpose4(scur[f][h]);
         }
       }
-      fr.load_scales8(sraw, kc / 8 + 1, nkc, lg, kbase);
+      fr.load_scales8(sraw, kc / 8 + 1, nkc, lg, kbase, kc + 8 >= nkc ? kPast : 0u);
 #pragma unroll
       for (int c8 = 0; c8 < 8; ++c8) {
         const int k = kc + c8;
         if (k >= nkc) break;
         if ((c8 & 1) == 0) {
           compute(wc0a, wc1a, slot0, c8);
-          fr.load_codes_rows(wc0a, wc1a, vrow, kbase + min(k + 2, last));
+          codes(wc0a, wc1a, k + 2);
           bstore(slot1, bq1a, bq1b);
-          bload(bq1a, bq1b, min(k + 3, last));
+          bload(bq1a, bq1b, k + 3);
         } else {
           compute(wc0b, wc1b, slot1, c8);
-          fr.load_codes_rows(wc0b, wc1b, vrow, kbase + min(k + 2, last));
+          codes(wc0b, wc1b, k + 2);
           bstore(slot0, bq0a, bq0b);
-          bload(bq0a, bq0b, min(k + 3, last));
+          bload(bq0a, bq0b, k + 3);
         }
       }
     }
@@ -595,14 +609,14 @@ void nvfp4_gemm_direct(const GemmArgs a) {
     // is refilled with the next chunk's step q right after use); NVFP4 rows
     // are double buffered like the weights.
     BBuf<AM> bb0, bb1;
-    auto bload = [&](BBuf<AM>& b, int kc) {
+    auto bload = [&](BBuf<AM>& b, int kc, uint32_t past = 0) {
       if constexpr (AM == A_F16) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) b.v[q] = buf_load16(rb, vb, kc * kChunk * 2 + q * 64);
+        for (int q = 0; q < 8; ++q) b.v[q] = buf_load16(rb, vb | past, kc * kChunk * 2 + q * 64);
       } else {
-        b.c0 = buf_load16(rb, vb, kc * 128);
-        b.c1 = buf_load16(rb, vb + 16, kc * 128);
-        b.s = buf_load4(rbs, vbs, kc * 16);
+        b.c0 = buf_load16(rb, vb | past, kc * 128);
+        b.c1 = buf_load16(rb, (vb + 16) | past, kc * 128);
+        b.s = buf_load4(rbs, vbs | past, kc * 16);
       }
     };
 
@@ -635,30 +649,31 @@ void nvfp4_gemm_direct(const GemmArgs a) {
     };
 
     // Prefetch: weights two chunks ahead (wb0 / wb1), B one chunk ahead.
-    // Chunk indices are clamped to the last chunk, so the loads past the end
-    // re-read it (in bounds, results unused) instead of branching.
+    // Requests past the end keep their place (no branch) but carry kPast:
+    // no memory access, results unused.
     const int last = nkc - 1;
     WBuf<R> wb0, wb1;
+    auto past = [&](int kc) { return kc > last ? kPast : 0u; };
     fr.load(wb0, 0);
     bload(bb0, 0);
-    fr.load(wb1, min(1, last));
-    if constexpr (AM == A_FP4) bload(bb1, min(1, last));
+    fr.load(wb1, min(1, last), past(1));
+    if constexpr (AM == A_FP4) bload(bb1, min(1, last), past(1));
     for (int kc = 0; kc < nkc; kc += 2) {
       if constexpr (AM == A_F16) {
         compute(wb0, bb0, min(kc + 1, last));
       } else {
         compute(wb0, bb0, 0);
-        bload(bb0, min(kc + 2, last));
+        bload(bb0, min(kc + 2, last), past(kc + 2));
       }
-      fr.load(wb0, min(kc + 2, last));
+      fr.load(wb0, min(kc + 2, last), past(kc + 2));
       if (kc + 1 >= nkc) break;
       if constexpr (AM == A_F16) {
         compute(wb1, bb0, min(kc + 2, last));
       } else {
         compute(wb1, bb1, 0);
-        bload(bb1, min(kc + 3, last));
+        bload(bb1, min(kc + 3, last), past(kc + 3));
       }
-      fr.load(wb1, min(kc + 3, last));
+      fr.load(wb1, min(kc + 3, last), past(kc + 3));
     }
     epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, min(it.m, pbase + 16), lr, lg);
   }
@@ -753,17 +768,19 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     // without a memory access).
     const int nsw = __builtin_amdgcn_readfirstlane((prow + RSTEP - 1) / RSTEP);
 
+    // kc past the end: no memory access (kPast)
     auto stage_load = [&](int kc) {
-      kc += kbase;
+      const uint32_t past = kc > last ? kPast : 0u;
+      kc = min(kc, last) + kbase;
 #pragma unroll
       for (int i = 0; i < SROWS; ++i) {
         if (DB && i >= nsw) break;
         if constexpr (AM == A_F16) {
-          st0[i] = buf_load16(ra, so[i], kc * kChunk * 2);
+          st0[i] = buf_load16(ra, so[i] | past, kc * kChunk * 2);
         } else {
-          st0[i] = buf_load16(ra, so[i], kc * 128);
-          st1[i] = buf_load16(ra, so[i], kc * 128 + 16);
-          sts[i] = buf_load4(ras, sso[i], kc * 16);
+          st0[i] = buf_load16(ra, so[i] | past, kc * 128);
+          st1[i] = buf_load16(ra, so[i] | past, kc * 128 + 16);
+          sts[i] = buf_load4(ras, sso[i] | past, kc * 16);
         }
       }
     };
@@ -811,19 +828,21 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     WBuf<R> wb, wb1;
     u32x4 sq[R];        // QUAD: scale words of the quad (raw, then transposed)
     uint32_t s3[R];     // QUAD: word of the quad's last chunk, while sq receives the next quad
-    auto load_quad = [&](int j) {   // raw scale bytes of quad j (chunks clamped to the last one)
+    auto load_quad = [&](int j, uint32_t past) {   // raw scale bytes of quad j (chunks clamped to the last one)
       const int k = min(4 * j + lg, last);
 #pragma unroll
-      for (int f = 0; f < R; ++f) sq[f] = buf_load16(fr.rs, fr.vs - lg * 4 + k * 16, fr.ss[f]);
+      for (int f = 0; f < R; ++f) sq[f] = buf_load16(fr.rs, (fr.vs - lg * 4 + k * 16) | past, fr.ss[f]);
     };
     const int lane_off = lr * kLdsRow + (AM == A_F16 ? lg * 16 : lg * 128);
     auto item_off = [&](int q, int c) {
       return c * 16 * kLdsRow + (AM == A_F16 ? q * 64 : q * 16);
     };
     // buf: LDS buffer = parity of the chunk; w: its weights; next_kc: chunk
-    // whose codes are requested into w while it is consumed (QUAD); j:
-    // position of the chunk in its quad (QUAD)
+    // whose codes are requested into w while it is consumed (QUAD; past the
+    // end: no memory access); j: position of the chunk in its quad (QUAD)
     auto compute = [&](int buf, WBuf<R>& w, int next_kc, int j) {
+      const uint32_t npast = next_kc > last ? kPast : 0u;
+      next_kc = min(next_kc, last);
       if constexpr (QUAD) {
         if (j == 0) {
 #pragma unroll
@@ -832,7 +851,7 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
           // the next quad's raw words go to sq, a chunk before they are needed
 #pragma unroll
           for (int f = 0; f < R; ++f) s3[f] = sq[f][3];
-          load_quad(next_kc / 4);
+          load_quad(next_kc / 4, npast);
           __builtin_amdgcn_sched_barrier(0);   // keep the requests here, a chunk ahead
         }
       }
@@ -868,11 +887,11 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         for (int f = 0; f < R; ++f) af[f] = decode8(word_of(w.c0[f], w.c1[f], q), sc[f][(q >> 1) & 1]);
         if (QUAD && q == 3) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) w.c0[f] = buf_load16(fr.rw, fr.vw, fr.sw[f] + next_kc * 128);
+          for (int f = 0; f < R; ++f) w.c0[f] = buf_load16(fr.rw, fr.vw | npast, fr.sw[f] + next_kc * 128);
         }
         if (QUAD && q == 7) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) w.c1[f] = buf_load16(fr.rw, fr.vw + 16, fr.sw[f] + next_kc * 128);
+          for (int f = 0; f < R; ++f) w.c1[f] = buf_load16(fr.rw, (fr.vw + 16) | npast, fr.sw[f] + next_kc * 128);
         }
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
@@ -886,10 +905,10 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       }
     };
 
-    // chunks past the end re-read the last chunk (in bounds, unused)
+    // requests for chunks past the end carry kPast (no memory access, unused)
     if constexpr (QUAD) {
       fr.load_codes(wb.c0, wb.c1, 0);
-      load_quad(0);
+      load_quad(0, 0u);
     } else {
       fr.load(wb, kbase);
     }
@@ -897,8 +916,8 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     stage_write(0);
     __syncthreads();
     // Even chunks in LDS buffer 0, odd ones in buffer 1; every chunk stages
-    // the next one (the last one again past the end: in bounds, into the
-    // buffer no wave reads any more).
+    // the next one (past the end: zeros, into the buffer no wave reads any
+    // more).
     if constexpr (QUAD) {
       // quads of chunks (the host uses this configuration when 4 divides
       // the chunk count)
@@ -915,8 +934,8 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         compute(0, wb, kc + 3, 2);
         stage_write(1);
         __syncthreads();
-        stage_load(min(kc + 4, last));
-        compute(1, wb, min(kc + 4, last), 3);
+        stage_load(kc + 4);
+        compute(1, wb, kc + 4, 3);
         stage_write(0);
         __syncthreads();
       }
@@ -935,9 +954,9 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         stage_write(1);
         __syncthreads();
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        stage_load(min(kc + 2, last));
-        fr.load(wb, kbase + min(kc + 2, last));
-        compute(1, wb1, min(kc + 2, last), 0);
+        stage_load(kc + 2);
+        fr.load(wb, kbase + min(kc + 2, last), kc + 2 > last ? kPast : 0u);
+        compute(1, wb1, kc + 2, 0);
         stage_write(0);
         __syncthreads();
       }
