@@ -87,12 +87,15 @@ __global__ __launch_bounds__(256) void nvfp4_router_logits(const uint16_t* x, co
   struct Step {
     u32x4 a[2], b[4];
   };
+  // steps past the end keep their place in the pipeline but carry an offset
+  // outside the buffer resources: zeros, no memory access (results unused)
   auto load = [&](int step, Step& st) {
-    const uint32_t off = (uint32_t)min(step, nsteps - 1) * 64;   // past the end: the last step again
+    const uint32_t past = step >= nsteps ? 0x80000000u : 0u;
+    const uint32_t off = (uint32_t)min(step, nsteps - 1) * 64;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) st.a[f] = buf_load16(rw, we[f], off);
+    for (int f = 0; f < 2; ++f) st.a[f] = buf_load16(rw, we[f] | past, off);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) st.b[c] = buf_load16(rx, xt[c], off);
+    for (int c = 0; c < 4; ++c) st.b[c] = buf_load16(rx, xt[c] | past, off);
   };
   auto mma = [&](const Step& st) {
     typedef short bf16x8 __attribute__((ext_vector_type(8)));
