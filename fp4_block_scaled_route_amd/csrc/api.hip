@@ -325,7 +325,14 @@ int nvfp4_rmsnorm_quantize(const void* x_bf16, const void* w_bf16, float eps, in
                            size_t workspace_bytes, void* stream) {
   if (T < 0 || K <= 0 || K % 16 != 0 || T >= kMaxDim || K >= kMaxDim || T * K >= kMaxDim) return NVFP4_ERR_SHAPE;
   if (!(eps > 0.0f) || eps == __builtin_inff()) return NVFP4_ERR_ARG;
-  if (T == 0) return NVFP4_OK;
+  if (T == 0) {
+    // nothing to normalise; a computed gs is that of no elements (0), as in nvfp4_quantize_act
+    if (!compute_gs) return NVFP4_OK;
+    if (!gs) return NVFP4_ERR_NULL;
+    if (!aligned(gs, 4)) return NVFP4_ERR_ALIGN;
+    return launch_status(launch_rmsnorm_quantize(nullptr, nullptr, eps, 0, K, nullptr, gs, 1, nullptr, nullptr,
+                                                 nullptr, static_cast<hipStream_t>(stream)));
+  }
   if (!x_bf16 || !w_bf16 || !gs || !x_fp4 || !x_sf) return NVFP4_ERR_NULL;
   if (!aligned(x_bf16, 16) || !aligned(w_bf16, 16) || !aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gs, 4) ||
       (y_bf16 && !aligned(y_bf16, 16)))

@@ -131,8 +131,8 @@ __global__ void nvfp4_rmsnorm_gs_finish(float* gs) { gs[0] = gs[0] / 2688.0f; }
 
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* w, float eps, int T, int K, uint16_t* y,
                                    float* gs, int compute_gs, uint8_t* q, uint8_t* sf, float* rrow, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
   if (compute_gs) hipLaunchKernelGGL(nvfp4_rmsnorm_gs_zero, dim3(1), dim3(1), 0, s, gs);
+  if (T <= 0) return hipGetLastError();
   hipLaunchKernelGGL(nvfp4_rmsnorm_stats, dim3((T + 3) / 4), dim3(256), 0, s, x, w, T, K, eps, rrow, y,
                      compute_gs ? gs : nullptr);
   const int64_t nblk = (int64_t)T * (K / 16);

@@ -153,16 +153,21 @@ def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
 
 
 def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, gs: Optional[torch.Tensor] = None,
-                     y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                     y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     gs_out: Optional[torch.Tensor] = None):
     """RMSNorm of bf16 rows x [T, K] with weight w [K], quantized to NVFP4.
     Returns (codes [T, K/2], scale bytes [T, K/16], gs [1]); gs is computed
-    unless given; ``y`` (bf16 [T, K]) receives the RMSNorm output if given."""
+    into ``gs_out`` (allocated if not given) unless given; ``y`` (bf16
+    [T, K]) receives the RMSNorm output if given."""
     t, k = x.shape
     dev = x.device
     q = torch.empty((t, k // 2), dtype=torch.uint8, device=dev)
     sf = torch.empty((t, k // 16), dtype=torch.uint8, device=dev)
     compute = gs is None
-    g = torch.zeros(1, dtype=torch.float32, device=dev) if compute else gs
+    if compute:
+        g = gs_out if gs_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        g = gs
     if workspace is None:
         workspace = torch.empty(max(16, lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size()

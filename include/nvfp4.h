@@ -35,7 +35,10 @@
  * Constraints (checked on the host before any launch):
  *   K and every reduction length % 256 == 0; output widths % 16 == 0;
  *   device pointers 16-byte aligned (scale and gs pointers 4-byte aligned);
- *   sizes positive and below 2^31 elements per dimension.
+ *   sizes positive and below 2^31 elements per dimension, except the row or
+ *   token count (M, T), which may be 0: the other sizes are still checked,
+ *   nothing is written (but the gs of a quantizer with compute_gs) and NULL
+ *   pointers are accepted.
  * Errors: a negative NVFP4_ERR_* code is returned and nothing is launched
  * when a check fails; NVFP4_ERR_LAUNCH reports a HIP launch error.  Values
  * inside device buffers (expert ids, NaN scales) are not checked on the host:
@@ -83,6 +86,8 @@ int nvfp4_abi_version(void);
  *   gs         device fp32 scalar: output when compute_gs != 0 (written with
  *              max|x| / 2688 computed on the device), input otherwise.
  *   x_fp4      [M, K/2] output codes; x_sf [M, K/16] output scale bytes.
+ * M == 0 writes nothing but gs, which compute_gs sets to 0 (no elements);
+ * x_bf16, x_fp4 and x_sf may then be NULL.
  * Requires K % 16 == 0 (K % 256 == 0 if the result feeds nvfp4_linear or
  * nvfp4_moe_grouped).
  */
@@ -101,6 +106,8 @@ int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int 
  *   gs, compute_gs, x_fp4 [T, K/2], x_sf [T, K/16]: as nvfp4_quantize_act,
  *   applied to y.
  *   workspace: nvfp4_rmsnorm_quantize_workspace_size(T) bytes (r per row).
+ * T == 0 writes nothing but gs, which compute_gs sets to 0 (no elements);
+ * every other pointer may then be NULL.
  * Requires K % 16 == 0 (K % 256 == 0 to feed nvfp4_linear), eps > 0 and
  * finite (NVFP4_ERR_ARG otherwise), 16-byte aligned tensors.
  */

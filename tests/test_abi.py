@@ -100,7 +100,10 @@ def test_rmsnorm_quantize_validation(lib):
     assert call(T=-1) == -2
     assert call(eps=0.0) == -6               # eps must be positive
     assert call(eps=float("nan")) == -6
-    assert call(T=0) == 0
+    assert call(T=0, comp=0) == 0            # empty batch, supplied gs: nothing to launch
+    assert call(T=0, x=None, w=None, q=None, sf=None, work=None, comp=0) == 0
+    assert call(T=0, gs=None) == -1          # empty batch still writes a computed gs
+    assert call(T=0, gs=ctypes.c_void_p(0x1002)) == -3
     assert call(w=None) == -1
     assert call(gs=None) == -1
     assert call(x=ctypes.c_void_p(0x1008)) == -3
