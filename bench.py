@@ -700,7 +700,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
-              "mode: the sharding design is described in DESIGN.md", file=sys.stderr)
+              "mode. It would shard by experts for prefill (each GPU owns E/G experts; token rows go "
+              "all-to-all before and after the grouped GEMMs) and over the intermediate size for decode "
+              "(each GPU streams 1/G of every touched expert; y is reduced)", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
