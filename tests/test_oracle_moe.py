@@ -5,7 +5,7 @@ import pytest
 
 from conftest import golden_dict
 from fp4_block_scaled_route_amd import synth
-from oracle import codec, moe
+from oracle import codec, moe, quant
 
 
 def test_permute_hand_worked():
@@ -151,3 +151,72 @@ def test_single_expert_equals_two_linears_and_silu():
     want = linear.linear_bf16(h, w2, s2, g2)
     got = moe.moe_forward(x, mi.topk_ids, np.ones_like(mi.topk_w), mi.experts.expert)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# fully-FP4 expert: h quantized with a2_gs before the down projection, and the
+# warm-up calibration of a2_gs (tests/golden/fp4_hidden_example.txt)
+# ---------------------------------------------------------------------------
+
+
+def _tie_point_expert():
+    """Case 2 of fp4_hidden_example.txt: g_i = 64 (silu exact), u_i = t_i / 64."""
+    g = golden_dict("fp4_hidden_example.txt")
+    w1c = np.zeros((32, 16), np.uint8)
+    s1 = np.full((32, 1), 0x38, np.uint8)
+    w1c[:16, 0] = 4                     # 2.0
+    s1[:16, 0] = 0x60                   # 32
+    w1c[16:, 0] = [int(v) for v in g["case2_up_codes"]]
+    s1[16:, 0] = [int(v, 16) for v in g["case2_up_bytes"]]
+    w2c = np.zeros((16, 16), np.uint8)
+    np.fill_diagonal(w2c, 2)
+    return (codec.pack_fp4(w1c), s1, 1.0, codec.pack_fp4(w2c), np.full((16, 1), 0x38, np.uint8), 1.0), g
+
+
+def _e0():
+    x = np.zeros((1, 16))
+    x[0, 0] = 1.0
+    return x
+
+
+def _deq(ex):
+    return codec.dequant_nvfp4(*ex[:3]), codec.dequant_nvfp4(*ex[3:])
+
+
+def test_fp4_hidden_one_hot_hand_worked():
+    g = golden_dict("fp4_hidden_example.txt")
+    w1d, w2d = _deq(_one_hot_swiglu_expert())
+    amax = moe.hidden_amax(_e0(), w1d)
+    assert amax == float(g["case1_hidden_amax"][0])
+    a2 = np.float32(np.float32(amax) / np.float32(2688.0))
+    assert a2 == np.float32(float(g["case1_a2_gs"][0]))
+    y = moe.expert_ffn(_e0(), w1d, w2d, a2_gs=a2)
+    assert np.array_equal(y[0], np.full(16, float(g["case1_y_all"][0])))
+    # the same through the MoE layer (E = 1, k = 1, w = 1)
+    ym = moe.moe_forward(_e0(), np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32),
+                         lambda e: _one_hot_swiglu_expert(), None, a2_gs=a2)
+    assert np.array_equal(ym[0], y[0])
+
+
+def test_fp4_hidden_tie_points_hand_worked():
+    ex, g = _tie_point_expert()
+    w1d, w2d = _deq(ex)
+    want_h = np.array([float(v) for v in g["case2_h"]])
+    # unquantized h: W2 is the identity, so y = h = t exactly
+    assert np.array_equal(moe.expert_ffn(_e0(), w1d, w2d)[0], want_h)
+    assert moe.hidden_amax(_e0(), w1d) == float(g["case2_hidden_amax"][0])
+    y = moe.expert_ffn(_e0(), w1d, w2d, a2_gs=np.float32(1.0))
+    assert np.array_equal(y[0], np.array([float(v) for v in g["case2_y"]]))
+    # the h quantization itself: one block, scale byte and tie-to-even codes
+    hp, hs, _ = quant.quantize_nvfp4(want_h[None].astype(np.float32), gs=np.float32(1.0))
+    assert hs[0, 0] == int(g["case2_scale_byte"][0], 16)
+    assert list(codec.unpack_fp4(hp)[0]) == [int(v) for v in g["case2_codes"]]
+    # two tokens routed to the tie-point expert and the one-hot one, with weights
+    x = np.vstack([_e0(), _e0()])
+    ids = np.array([[0, 1], [1, 0]], np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.5]], np.float32)
+    experts = {0: ex, 1: _one_hot_swiglu_expert()}
+    ym = moe.moe_forward(x, ids, w, lambda e: experts[e], None, a2_gs=np.float32(1.0))
+    y1 = moe.expert_ffn(_e0(), *_deq(experts[1]), a2_gs=np.float32(1.0))[0]
+    assert np.array_equal(ym[0], 0.75 * y[0] + 0.25 * y1)
+    assert np.array_equal(ym[1], 0.5 * y1 + 0.5 * y[0])

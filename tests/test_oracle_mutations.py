@@ -115,3 +115,51 @@ def test_routing_weights_before_down_projection_not_distinguishable_is_caught(mo
         return orig(x, ids, np.asarray(w)[:, ::-1], ew, sw, a2_gs, tokens)
     monkeypatch.setattr(moe, "moe_forward", wrong)
     _must_fail(tm.test_zeroing_a_weight_removes_exactly_that_pair)
+
+
+def _mutated_ffn(hidden):
+    """expert_ffn with its h step replaced by ``hidden(h, a2_gs)``."""
+    def ffn(a, w1d, w2d, a2_gs=None):
+        i = w1d.shape[0] // 2
+        h = moe.silu(a @ w1d[:i].T) * (a @ w1d[i:].T)
+        if a2_gs is not None:
+            h = hidden(h, a2_gs)
+        return h @ w2d.T
+    return ffn
+
+
+_FP4_HIDDEN_PINS = (tm.test_fp4_hidden_one_hot_hand_worked, tm.test_fp4_hidden_tie_points_hand_worked)
+
+
+def test_hidden_dequantized_with_doubled_scale(monkeypatch):
+    # h dequantized with 2 * a2_gs (a global scale applied twice)
+    def twice(h, gs):
+        hp, hs, g = quant.quantize_nvfp4(h.astype(np.float32), gs=gs)
+        return quant.dequantize_nvfp4(hp, hs, np.float32(2 * g))
+    monkeypatch.setattr(moe, "expert_ffn", _mutated_ffn(twice))
+    _must_fail(*_FP4_HIDDEN_PINS)
+
+
+def test_hidden_not_quantized(monkeypatch):
+    # a2_gs given but h passed to the down projection unquantized
+    monkeypatch.setattr(moe, "expert_ffn", _mutated_ffn(lambda h, gs: h))
+    _must_fail(*_FP4_HIDDEN_PINS)
+
+
+def test_hidden_global_scale_inverted(monkeypatch):
+    # page "commit 4c6464e": the global scale used inverted
+    def inverted(h, gs):
+        hp, hs, g = quant.quantize_nvfp4(h.astype(np.float32), gs=np.float32(1.0 / gs))
+        return quant.dequantize_nvfp4(hp, hs, g)
+    monkeypatch.setattr(moe, "expert_ffn", _mutated_ffn(inverted))
+    _must_fail(tm.test_fp4_hidden_one_hot_hand_worked)
+
+
+def test_hidden_amax_without_swiglu(monkeypatch):
+    # calibration amax taken over the gate * up product instead of silu(gate) * up
+    def amax(a, w1d):
+        i = w1d.shape[0] // 2
+        h = (a @ w1d[:i].T) * (a @ w1d[i:].T)
+        return float(np.max(np.abs(h.astype(np.float32)))) if h.size else 0.0
+    monkeypatch.setattr(moe, "hidden_amax", amax)
+    _must_fail(tm.test_fp4_hidden_one_hot_hand_worked)
