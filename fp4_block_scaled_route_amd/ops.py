@@ -62,6 +62,65 @@ class MoeArgs(ctypes.Structure):
     ]
 
 
+# ---------------------------------------------------------------------------
+# argument checks: the C ABI takes raw pointers and cannot see dtypes, shapes,
+# strides or devices, so every tensor is checked here before its pointer is
+# passed: dtypes, shapes (consistent with the sizes the call derives from its
+# weights and ids) and contiguity of all arguments first, then that they all
+# live on one GPU.  Size rules (multiples of 256, ranges) are the library's
+# own checks, reported as Nvfp4Error.
+# ---------------------------------------------------------------------------
+
+_U8, _I32, _F32, _BF16 = torch.uint8, torch.int32, torch.float32, torch.bfloat16
+SCALAR = "scalar"   # shape spec: a one-element tensor
+
+
+def _validate(specs):
+    """specs: (name, tensor or None, dtype, shape, required).  ``shape`` is a
+    tuple (exact), SCALAR (one element) or ("min", n) (1-D with at least n
+    elements).  Returns the device shared by the given tensors (None if none)."""
+    given = []
+    for name, t, dtype, shape, required in specs:
+        if t is None:
+            if required:
+                raise ValueError(f"{name} is required")
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            hint = " (call .int() on the ids)" if dtype == _I32 and t.dtype == torch.int64 else ""
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}{hint}")
+        if shape == SCALAR:
+            if t.numel() != 1:
+                raise ValueError(f"{name} must hold exactly one element, has {t.numel()}")
+        elif isinstance(shape, tuple) and len(shape) == 2 and shape[0] == "min":
+            if t.dim() != 1 or t.numel() < shape[1]:
+                raise ValueError(f"{name} must be 1-D with at least {shape[1]} elements, "
+                                 f"has shape {tuple(t.shape)}")
+        elif tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        given.append((name, t))
+    dev = None
+    for name, t in given:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _one_of(bf16_name, bf16, fp4_names, fp4):
+    """Exactly one activation form: the bf16 tensor, or all the NVFP4 parts."""
+    if (bf16 is None) == all(v is None for v in fp4):
+        raise ValueError(f"pass either {bf16_name} or {' + '.join(fp4_names)}")
+    if bf16 is None and any(v is None for v in fp4):
+        raise ValueError(f"NVFP4 activations need all of {', '.join(fp4_names)}")
+
+
 _lib = None
 
 
@@ -120,8 +179,8 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else _c_ptr(t.data_ptr())
 
 
-def _stream():
-    return _c_ptr(torch.cuda.current_stream().cuda_stream)
+def _stream(dev=None):
+    return _c_ptr(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def status_string(status: int) -> str:
@@ -137,18 +196,22 @@ def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
     computed on the device (max|x| / 2688) into ``gs_out`` (allocated if not
     given) and returned; otherwise ``gs`` (a 1-element fp32 device tensor) is
     used.  Returns (codes [M,K/2] u8, scales [M,K/16] u8, gs [1] fp32)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [M, K]")
     m, k = x.shape
+    q, sf = out if out is not None else (None, None)
+    dev = _validate([("x", x, _BF16, (m, k), True), ("gs", gs, _F32, SCALAR, False),
+                     ("out[0]", q, _U8, (m, k // 2), False), ("out[1]", sf, _U8, (m, k // 16), False),
+                     ("gs_out", gs_out, _F32, SCALAR, False)])
     if out is None:
-        q = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
-        sf = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
-    else:
-        q, sf = out
+        q = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        sf = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
     compute = gs is None
     if compute:
-        gsb = gs_out if gs_out is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+        gsb = gs_out if gs_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
     else:
         gsb = gs
-    _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _stream()))
+    _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _stream(dev)))
     return q, sf, gsb
 
 
@@ -159,8 +222,12 @@ def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, gs: Optional[
     Returns (codes [T, K/2], scale bytes [T, K/16], gs [1]); gs is computed
     into ``gs_out`` (allocated if not given) unless given; ``y`` (bf16
     [T, K]) receives the RMSNorm output if given."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [T, K]")
     t, k = x.shape
-    dev = x.device
+    dev = _validate([("x", x, _BF16, (t, k), True), ("w", w, _BF16, (k,), True),
+                     ("gs", gs, _F32, SCALAR, False), ("y", y, _BF16, (t, k), False),
+                     ("workspace", workspace, _U8, ("min", 1), False), ("gs_out", gs_out, _F32, SCALAR, False)])
     q = torch.empty((t, k // 2), dtype=torch.uint8, device=dev)
     sf = torch.empty((t, k // 16), dtype=torch.uint8, device=dev)
     compute = gs is None
@@ -169,10 +236,11 @@ def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, gs: Optional[
     else:
         g = gs
     if workspace is None:
-        workspace = torch.empty(max(16, lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8, device=dev)
-    wsb = workspace.numel() * workspace.element_size()
+        workspace = torch.empty(max(16, lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8,
+                                device=dev)
+    wsb = workspace.numel()
     _check(lib().nvfp4_rmsnorm_quantize(_p(x), _p(w), float(eps), t, k, _p(y), _p(g), int(compute), _p(q), _p(sf),
-                                        _p(workspace), wsb, _stream()))
+                                        _p(workspace), wsb, _stream(dev)))
     return q, sf, g
 
 
@@ -182,17 +250,28 @@ def linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Optional[t
            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[M, N] = x @ W^T (bf16 out).  Activations: ``x`` bf16 [M, K], or
     ``x_fp4`` [M, K/2] + ``x_sf`` [M, K/16] + ``gsa`` [1]."""
-    n = w.shape[0]
-    k = w.shape[1] * 2
-    m = (x if x is not None else x_fp4).shape[0]
-    dev = w.device
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("w must be a 2-D tensor [N, K/2]")
+    n, k = w.shape[0], w.shape[1] * 2
+    _one_of("x", x, ("x_fp4", "x_sf", "gsa"), (x_fp4, x_sf, gsa))
+    act = x if x is not None else x_fp4
+    if act.dim() != 2:
+        raise ValueError("activations must be 2-D [M, K] (NVFP4: [M, K/2])")
+    m = act.shape[0]
+    dev = _validate([("w", w, _U8, (n, k // 2), True), ("w_sf", w_sf, _U8, (n, k // 16), True),
+                     ("ws2", ws2, _F32, SCALAR, True),
+                     ("x", x, _BF16, (m, k), False), ("x_fp4", x_fp4, _U8, (m, k // 2), False),
+                     ("x_sf", x_sf, _U8, (m, k // 16), False), ("gsa", gsa, _F32, SCALAR, False),
+                     ("out", out, _BF16, (m, n), False), ("workspace", workspace, _U8, ("min", 0), False)])
     need = lib().nvfp4_linear_workspace_size(m, n, k)
+    if workspace is not None and workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wsb = workspace.numel() if workspace is not None else 0
     _check(lib().nvfp4_linear(_p(x), _p(x_fp4), _p(x_sf), _p(gsa), _p(w), _p(w_sf), _p(ws2),
-                              m, n, k, _p(y), _p(workspace), wsb, _stream()))
+                              m, n, k, _p(y), _p(workspace), wsb, _stream(dev)))
     return y
 
 
@@ -207,22 +286,70 @@ def grouped_linear(w: torch.Tensor, w_sf: torch.Tensor, ws2: torch.Tensor, x: Op
     """y[T, G, N] with y[:, g] = x[:, g] @ W[g]^T (bf16 out).  Weights
     ``w`` [G, N, K/2], ``w_sf`` [G, N, K/16], ``ws2`` [G].  Activations: ``x``
     bf16 [T, G, K], or ``x_fp4`` [T, G, K/2] + ``x_sf`` [T, G, K/16] + ``gsa`` [1]."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 3:
+        raise ValueError("w must be a 3-D tensor [G, N, K/2]")
     g, n, kh = w.shape
     k = kh * 2
-    t = (x if x is not None else x_fp4).shape[0]
-    dev = w.device
-    y = out if out is not None else torch.empty((t, g, n), dtype=torch.bfloat16, device=dev)
+    _one_of("x", x, ("x_fp4", "x_sf", "gsa"), (x_fp4, x_sf, gsa))
+    act = x if x is not None else x_fp4
+    if act.dim() != 3:
+        raise ValueError("activations must be 3-D [T, G, K] (NVFP4: [T, G, K/2])")
+    t = act.shape[0]
+    dev = _validate([("w", w, _U8, (g, n, k // 2), True), ("w_sf", w_sf, _U8, (g, n, k // 16), True),
+                     ("ws2", ws2, _F32, (g,), True),
+                     ("x", x, _BF16, (t, g, k), False), ("x_fp4", x_fp4, _U8, (t, g, k // 2), False),
+                     ("x_sf", x_sf, _U8, (t, g, k // 16), False), ("gsa", gsa, _F32, SCALAR, False),
+                     ("out", out, _BF16, (t, g, n), False), ("workspace", workspace, _U8, ("min", 0), False)])
     need = lib().nvfp4_grouped_linear_workspace_size(t, g, n, k)
+    if workspace is not None and workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    y = out if out is not None else torch.empty((t, g, n), dtype=torch.bfloat16, device=dev)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wsb = workspace.numel() if workspace is not None else 0
     _check(lib().nvfp4_grouped_linear(_p(x), _p(x_fp4), _p(x_sf), _p(gsa), _p(w), _p(w_sf), _p(ws2),
-                                      t, g, n, k, _p(y), _p(workspace), wsb, _stream()))
+                                      t, g, n, k, _p(y), _p(workspace), wsb, _stream(dev)))
     return y
 
 
 def moe_workspace_size(t: int, h: int, i: int, e: int, topk: int, has_shared: bool, h_fp4: bool) -> int:
     return int(lib().nvfp4_moe_workspace_size(t, h, i, e, topk, int(has_shared), int(h_fp4)))
+
+
+def _moe_specs(topk_ids, topk_w, w1, w1_sf, w1_ws2, w2, w2_sf, w2_ws2, x, x_fp4, x_sf, a1_gs, shared,
+               a2_gs, a2_gs_out, workspace, offsets_out, perm_out, out):
+    """Shape (T, H, I, E, topk) of a MoE call and the checks of its tensors."""
+    for name, t, dim in (("topk_ids", topk_ids, 2), ("w1", w1, 3)):
+        if not isinstance(t, torch.Tensor) or t.dim() != dim:
+            raise ValueError(f"{name} must be a {dim}-D tensor")
+    e, two_i, h_half = w1.shape
+    if two_i % 2:
+        raise ValueError(f"w1 has {two_i} rows per expert; gate and up need an even count")
+    h, i = h_half * 2, two_i // 2
+    t, topk = topk_ids.shape
+    _one_of("x", x, ("x_fp4", "x_sf", "a1_gs"), (x_fp4, x_sf, a1_gs))
+    if shared is not None and len(shared) != 6:
+        raise ValueError("shared must be (s1, s1_sf, s1_ws2, s2, s2_sf, s2_ws2)")
+    s = shared if shared is not None else (None,) * 6
+    has = shared is not None
+    specs = [
+        ("topk_ids", topk_ids, _I32, (t, topk), True), ("topk_w", topk_w, _F32, (t, topk), True),
+        ("w1", w1, _U8, (e, 2 * i, h // 2), True), ("w1_sf", w1_sf, _U8, (e, 2 * i, h // 16), True),
+        ("w1_ws2", w1_ws2, _F32, (e,), True),
+        ("w2", w2, _U8, (e, h, i // 2), True), ("w2_sf", w2_sf, _U8, (e, h, i // 16), True),
+        ("w2_ws2", w2_ws2, _F32, (e,), True),
+        ("x", x, _BF16, (t, h), False), ("x_fp4", x_fp4, _U8, (t, h // 2), False),
+        ("x_sf", x_sf, _U8, (t, h // 16), False), ("a1_gs", a1_gs, _F32, SCALAR, False),
+        ("shared[0] (s1)", s[0], _U8, (2 * i, h // 2), has), ("shared[1] (s1_sf)", s[1], _U8, (2 * i, h // 16), has),
+        ("shared[2] (s1_ws2)", s[2], _F32, SCALAR, has),
+        ("shared[3] (s2)", s[3], _U8, (h, i // 2), has), ("shared[4] (s2_sf)", s[4], _U8, (h, i // 16), has),
+        ("shared[5] (s2_ws2)", s[5], _F32, SCALAR, has),
+        ("a2_gs", a2_gs, _F32, SCALAR, False), ("a2_gs_out", a2_gs_out, _F32, SCALAR, False),
+        ("workspace", workspace, _U8, ("min", 0), False),
+        ("offsets_out", offsets_out, _I32, (e + 2,), False), ("perm_out", perm_out, _I32, (t * topk + t,), False),
+        ("out", out, _BF16, (t, h), False),
+    ]
+    return (t, h, i, e, topk), specs
 
 
 def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
@@ -238,15 +365,17 @@ def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
                 out: Optional[torch.Tensor] = None, stage_events: Optional[Sequence[int]] = None) -> torch.Tensor:
     """One MoE layer (see nvfp4_moe_grouped in include/nvfp4.h).
     ``shared`` = (s1, s1_sf, s1_ws2, s2, s2_sf, s2_ws2) or None."""
-    e, two_i, h_half = w1.shape
-    h = h_half * 2
-    i = two_i // 2
-    t, topk = topk_ids.shape
-    dev = w1.device
+    (t, h, i, e, topk), specs = _moe_specs(topk_ids, topk_w, w1, w1_sf, w1_ws2, w2, w2_sf, w2_ws2, x, x_fp4, x_sf,
+                                           a1_gs, shared, a2_gs, a2_gs_out, workspace, offsets_out, perm_out, out)
+    dev = _validate(specs)
+    need = moe_workspace_size(t, h, i, e, topk, shared is not None, a2_gs is not None)
+    if workspace is not None and workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    if stage_events is not None and len(stage_events) != 8:
+        raise ValueError("stage_events must hold 8 hipEvent_t handles (0 to skip one)")
     y = out if out is not None else torch.empty((t, h), dtype=torch.bfloat16, device=dev)
     if workspace is None:
-        workspace = torch.empty(moe_workspace_size(t, h, i, e, topk, shared is not None, a2_gs is not None),
-                                dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     a = MoeArgs()
     a.T, a.H, a.I, a.E, a.topk = t, h, i, e, topk
     a.x, a.x_fp4, a.x_sf, a.a1_gs = _p(x), _p(x_fp4), _p(x_sf), _p(a1_gs)
@@ -259,13 +388,13 @@ def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
         a.s1, a.s1_sf, a.s1_ws2 = _p(s1), _p(s1_sf), _p(s1_ws2)
         a.s2, a.s2_sf, a.s2_ws2 = _p(s2), _p(s2_sf), _p(s2_ws2)
     a.workspace = _p(workspace)
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.workspace_bytes = workspace.numel()
     a.offsets_out, a.perm_out = _p(offsets_out), _p(perm_out)
     a.y = _p(y)
     if stage_events is not None:
         arr = (_c_ptr * len(stage_events))(*[_c_ptr(int(v)) for v in stage_events])
         a.stage_events = ctypes.cast(arr, ctypes.POINTER(_c_ptr))
-    _check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream()))
+    _check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream(dev)))
     return y
 
 
@@ -273,10 +402,14 @@ def router_prepare(w: torch.Tensor, out: Optional[torch.Tensor] = None,
                    scale_out: Optional[torch.Tensor] = None):
     """FP8-E4M3 round trip of a bf16 router weight [E, H] (see
     nvfp4_router_prepare).  Returns (w_rt bf16 [E, H], scale fp32 [1])."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("w must be a 2-D tensor [E, H]")
     e, h = w.shape
+    dev = _validate([("w", w, _BF16, (e, h), True), ("out", out, _BF16, (e, h), False),
+                     ("scale_out", scale_out, _F32, SCALAR, False)])
     w_rt = out if out is not None else torch.empty_like(w)
-    scale = scale_out if scale_out is not None else torch.empty(1, dtype=torch.float32, device=w.device)
-    _check(lib().nvfp4_router_prepare(_p(w), e, h, _p(scale), _p(w_rt), _stream()))
+    scale = scale_out if scale_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    _check(lib().nvfp4_router_prepare(_p(w), e, h, _p(scale), _p(w_rt), _stream(dev)))
     return w_rt, scale
 
 
@@ -289,15 +422,23 @@ def router_topk(x: torch.Tensor, w_rt: torch.Tensor, topk: int, logits: Optional
                 workspace: Optional[torch.Tensor] = None):
     """Router logits and top-k softmax (see nvfp4_router_topk).
     Returns (logits fp32 [T, E], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    for name, v in (("x", x), ("w_rt", w_rt)):
+        if not isinstance(v, torch.Tensor) or v.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
     t, h = x.shape
     e = w_rt.shape[0]
-    dev = x.device
+    dev = _validate([("x", x, _BF16, (t, h), True), ("w_rt", w_rt, _BF16, (e, h), True),
+                     ("logits", logits, _F32, (t, e), False), ("ids", ids, _I32, (t, topk), False),
+                     ("weights", weights, _F32, (t, topk), False),
+                     ("workspace", workspace, _U8, ("min", 0), False)])
+    need = router_workspace_size(t, h, e)
+    if workspace is not None and workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
     logits = logits if logits is not None else torch.empty((t, e), dtype=torch.float32, device=dev)
     ids = ids if ids is not None else torch.empty((t, topk), dtype=torch.int32, device=dev)
     weights = weights if weights is not None else torch.empty((t, topk), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(1, router_workspace_size(t, h, e)), dtype=torch.uint8, device=dev)
-    wsb = workspace.numel() * workspace.element_size()
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
     _check(lib().nvfp4_router_topk(_p(x), _p(w_rt), t, h, e, topk, _p(logits), _p(ids), _p(weights),
-                                   _p(workspace), wsb, _stream()))
+                                   _p(workspace), workspace.numel(), _stream(dev)))
     return logits, ids, weights

@@ -34,12 +34,20 @@ def test_moe_zero_tokens():
 
 
 def test_moe_zero_tokens_still_checks_shapes():
+    """The library's own size check at T = 0, called through the C ABI (the
+    binding would reject the inconsistent tensors before the call)."""
     mi, de, ds = _moe_inputs()
-    args = de.args()
-    args["w1"] = args["w1"][:, :, :100]   # hidden 200: not a multiple of 256
-    with pytest.raises(ops.Nvfp4Error) as e:
-        ops.moe_grouped(dev(mi.topk_ids[:0]), dev(mi.topk_w[:0]), **args, x=dev(mi.x[:0]))
-    assert e.value.status == -2
+    a = ops.MoeArgs()
+    a.T, a.H, a.I, a.E, a.topk = 0, 200, 256, 8, 2     # hidden 200: not a multiple of 256
+    a.x = de.w1.data_ptr()
+    a.topk_ids, a.topk_w = de.w1.data_ptr(), de.w1.data_ptr()
+    a.w1, a.w1_sf, a.w1_ws2 = de.w1.data_ptr(), de.w1_sf.data_ptr(), de.w1_ws2.data_ptr()
+    a.w2, a.w2_sf, a.w2_ws2 = de.w2.data_ptr(), de.w2_sf.data_ptr(), de.w2_ws2.data_ptr()
+    a.y = de.w1.data_ptr()
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    import ctypes
+    assert ops.lib().nvfp4_moe_grouped(ctypes.byref(a), None) == -2
 
 
 def test_router_zero_tokens():
