@@ -99,7 +99,7 @@ def hidden_amax(a: np.ndarray, w1d: np.ndarray) -> float:
 
 
 def moe_forward(x_rows, topk_ids, topk_w, expert_weights, shared_weights=None,
-                a2_gs=None, tokens=None):
+                a2_gs=None, tokens=None, workers=1, hook=None):
     """y[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x_t) + FFN_shared(x_t), float64.
 
     x_rows:   [T, H] float64 activations as the experts see them (bf16 values,
@@ -109,6 +109,16 @@ def moe_forward(x_rows, topk_ids, topk_w, expert_weights, shared_weights=None,
     shared_weights: same tuple for the shared expert, or None.
     tokens:   subset of token indices to compute (default: all).  Experts are
               dequantized one at a time to bound host memory.
+    workers:  experts evaluated concurrently by that many threads (each expert's
+              result is independent; the combine below runs afterwards in
+              the fixed order, so the result does not depend on it).
+    hook:     optional callable hook(e, rows, a, w1d, w2d, o) run once per
+              evaluated expert (e = -1 for the shared expert) with the output
+              positions ``rows`` (index into ``tokens``) and j of its pairs
+              (j = -1 for the shared expert), its input rows ``a``, its
+              dequantized weights and its output rows ``o``; test code uses it
+              to derive error bounds
+              from the same weights.  It must not modify its arguments.
     Returns y [len(tokens), H] float64 in the order of ``tokens``."""
     ids = np.asarray(topk_ids)
     w = np.asarray(topk_w, dtype=np.float64)
@@ -126,7 +136,8 @@ def moe_forward(x_rows, topk_ids, topk_w, expert_weights, shared_weights=None,
     # over j runs in order j = 0..k-1 for every token
     k = ids.shape[1]
     outs = np.zeros((len(tokens), k, h_dim), dtype=np.float64)
-    for e in sorted(uses):
+
+    def one_expert(e):
         w1, s1, g1, w2, s2, g2 = expert_weights(e)
         w1d = codec.dequant_nvfp4(w1, s1, g1)
         w2d = codec.dequant_nvfp4(w2, s2, g2)
@@ -135,12 +146,25 @@ def moe_forward(x_rows, topk_ids, topk_w, expert_weights, shared_weights=None,
         o = expert_ffn(a, w1d, w2d, a2_gs)
         for n, (yi, _, j) in enumerate(rows):
             outs[yi, j] = o[n]
-        del w1d, w2d
+        if hook is not None:
+            hook(e, [(yi, j) for (yi, _, j) in rows], a, w1d, w2d, o)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one_expert, sorted(uses)))
+    else:
+        for e in sorted(uses):
+            one_expert(e)
     for j in range(k):
         y += w[tokens, j][:, None] * outs[:, j]
     if shared_weights is not None:
         w1, s1, g1, w2, s2, g2 = shared_weights
         w1d = codec.dequant_nvfp4(w1, s1, g1)
         w2d = codec.dequant_nvfp4(w2, s2, g2)
-        y += expert_ffn(np.asarray(x_rows[tokens], dtype=np.float64), w1d, w2d, a2_gs)
+        a = np.asarray(x_rows[tokens], dtype=np.float64)
+        o = expert_ffn(a, w1d, w2d, a2_gs)
+        y += o
+        if hook is not None:
+            hook(-1, [(yi, -1) for yi in range(len(tokens))], a, w1d, w2d, o)
     return y

@@ -75,3 +75,53 @@ def full_size_experts(seed=0, h=7168, i=2048, e=384):
         shared = synth.make_experts(1, h, i, seed, synth._SHARED)
         _FULL[key] = (DeviceExperts(routed), DeviceExperts(shared))
     return _FULL[key]
+
+
+def calibrate_a2(xa, ids, host, tokens, shared_host=None, workers=16):
+    """Oracle-side warm-up calibration of the hidden activations' global
+    scale: max |h| over the pairs of ``tokens`` / 2688 (float32), each
+    expert's W1 dequantized once."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import codec, moe
+    rows = {}
+    for t in tokens:
+        for j in range(ids.shape[1]):
+            rows.setdefault(int(ids[t, j]), []).append(int(t))
+
+    def one(e):
+        src = host.expert(e) if e >= 0 else shared_host.expert(0)
+        r = rows[e] if e >= 0 else [int(t) for t in tokens]
+        return moe.hidden_amax(np.asarray(xa[r], dtype=np.float64), codec.dequant_nvfp4(*src[:3]))
+
+    keys = sorted(rows) + ([-1] if shared_host is not None else [])
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        amax = max(ex.map(one, keys))
+    return np.float32(np.float32(amax) / np.float32(2688.0))
+
+
+def covering_tokens(ids, n_experts, extra=(), seed=0, per_expert=1):
+    """Tokens whose routed experts cover every expert (greedy set cover over
+    a seeded shuffle of the batch), plus ``extra``; sorted."""
+    rng = np.random.default_rng(seed)
+    need = {e: per_expert for e in range(n_experts)}
+    chosen = set(int(v) for v in extra)
+    for t in chosen:
+        for e in ids[t]:
+            if need.get(int(e), 0) > 0:
+                need[int(e)] -= 1
+    for t in rng.permutation(ids.shape[0]):
+        if not any(v > 0 for v in need.values()):
+            break
+        gain = sum(1 for e in ids[t] if need.get(int(e), 0) > 0)
+        if gain >= 2 or (gain == 1 and len(chosen) > 4 * n_experts // ids.shape[1]):
+            chosen.add(int(t))
+            for e in ids[t]:
+                if need.get(int(e), 0) > 0:
+                    need[int(e)] -= 1
+    for e, v in need.items():   # any expert still missing: its first token
+        if v > 0:
+            chosen.add(int(np.nonzero((ids == e).any(axis=1))[0][0]))
+    return sorted(chosen)

@@ -5,6 +5,7 @@ import torch
 
 from gpu_util import compare, dev, f32, say
 from fp4_block_scaled_route_amd import ops, synth
+from moe_bound import check_elementwise, linear_reference_and_bound
 from oracle import linear, quant
 
 pytestmark = pytest.mark.gpu
@@ -27,8 +28,9 @@ def test_linear_bf16(m, n, k):
     li = synth.make_linear(m, n, k, seed=0)
     y = _run_bf16(li)
     torch.cuda.synchronize()
-    ref = linear.linear_bf16(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
+    ref, bound = linear_reference_and_bound(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
     compare(y, ref, what=f"linear {m}x{n}x{k}")
+    check_elementwise(y.float().cpu().numpy(), ref, bound, what=f"linear {m}x{n}x{k}")
 
 
 def test_linear_hand_worked_golden():
@@ -68,6 +70,33 @@ def test_linear_extreme_activation_range():
     assert not y[2].float().abs().sum()
 
 
+@pytest.mark.parametrize("m,k", [(4, 1536), (1, 7168)])
+def test_linear_wide_binade_spread_within_a_row(m, k):
+    """Rows whose magnitudes span more than 29 binades: the fp16 staging
+    shifts each row so its maximum lands in [2^14, 2^15), so elements more
+    than 29 binades below the maximum fall on fp16 subnormals (or flush to
+    zero below 2^-24 after the shift).  Each output element stays within its
+    bound, which carries 2^-39 * max|x_row| * sum_k |W[n, k]| for that
+    rounding besides the accumulation and output roundings."""
+    say(f"linear binade spread M={m} K={k}")
+    li = synth.make_linear(m, 256, k, seed=5)
+    x = li.x.float()
+    rng = np.random.default_rng(5)
+    for r in range(m):
+        # per element a power of two between 2^-34 and 2^6: a 40-binade spread
+        x[r] *= torch.from_numpy(np.exp2(rng.integers(-34, 7, size=k)).astype(np.float32))
+    li.x = x.to(torch.bfloat16)
+    xr = synth.bf16_to_float64(li.x)
+    mx = np.abs(xr).max(axis=1)
+    tiny = np.abs(xr) < mx[:, None] * 2.0 ** -29
+    assert tiny.sum(axis=1).min() > k // 10, "rows must hold elements below the exact staging range"
+    y = _run_bf16(li)
+    torch.cuda.synchronize()
+    ref, bound = linear_reference_and_bound(xr, li.w, li.w_sf, li.ws2)
+    compare(y, ref, what=f"binade spread {m}x{k}")
+    check_elementwise(y.float().cpu().numpy(), ref, bound, what=f"binade spread {m}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(8, 128, 256), (128, 1536, 7168), (33, 256, 1536)])
 def test_linear_nvfp4_activations(m, n, k):
     say(f"linear nvfp4 M={m} N={n} K={k}")
@@ -78,6 +107,8 @@ def test_linear_nvfp4_activations(m, n, k):
     rq, rs, rgs = quant.quantize_nvfp4(li.x.float().numpy())
     ref = linear.linear_nvfp4(rq, rs, rgs, li.w, li.w_sf, li.ws2)
     compare(y, ref, what="nvfp4 x nvfp4")
+    _, bound = linear_reference_and_bound(quant.dequantize_nvfp4(rq, rs, rgs), li.w, li.w_sf, li.ws2, x_fp4=True)
+    check_elementwise(y.float().cpu().numpy(), ref, bound, what="nvfp4 x nvfp4")
 
 
 def test_linear_empty_and_errors():
