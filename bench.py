@@ -7,11 +7,17 @@ A step is one pass of the whole hot path over one batch of seeded synthetic
 input that is already resident in HBM: for the MoE workloads one
 nvfp4_moe_grouped call (permute, gate/up GEMM + SwiGLU, down GEMM + scatter,
 weighted combine), preceded by nvfp4_quantize_act on the fully-FP4 workload.
-Prints ONE JSON line.  `value` is the step's algorithmic HBM throughput
-(bytes of every touched expert's NVFP4 weights and scales + activations in +
-output out, per second); TFLOP/s is reported beside it.  The roofline object
-describes the dominant kernel (the gate/up GEMM), timed with HIP events
-recorded around it on the stream it runs on.
+Prints ONE JSON line.
+
+Default (no --workload): the headline line is the fully-FP4 MoE batch (4096
+tokens, both GEMMs on NVFP4 activations), the configuration at the bf16
+MFMA ridge: `value` is its step throughput in TFLOP/s, reported with and
+without the activation quantizer; the MoE decode step (64 tokens) and
+prefill chunk (128 tokens, Zipf routing) are nested under "configs", each
+with its own ms_per_step, roofline and CPU oracle baseline.  All three use
+the same 384-expert stack.  The roofline objects describe each step's
+dominant kernel (the gate/up GEMM), timed with HIP events recorded around it
+on the stream it runs on.
 """
 
 from __future__ import annotations
@@ -129,30 +135,49 @@ def read_traffic(workload, src_hash):
 # ---------------------------------------------------------------------------
 
 
-def setup_moe(cfg, seed):
+class ExpertStack:
+    """One layer's routed experts and shared expert, on the host (for the
+    oracle) and on the device; shared by every MoE workload of a run."""
+
+    def __init__(self, cfg, seed):
+        import numpy as np
+        import torch
+
+        from fp4_block_scaled_route_amd import synth
+
+        t0 = time.time()
+        self.key = (cfg["E"], cfg["H"], cfg["I"], seed)
+        self.routed = synth.make_experts(cfg["E"], cfg["H"], cfg["I"], seed, 0)
+        self.shared = synth.make_experts(1, cfg["H"], cfg["I"], seed, synth._SHARED)
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+        ex, s = self.routed, self.shared
+        self.dev = dict(w1=d(ex.w1), w1_sf=d(ex.w1_sf), w1_ws2=d(ex.w1_ws2),
+                        w2=d(ex.w2), w2_sf=d(ex.w2_sf), w2_ws2=d(ex.w2_ws2))
+        self.shared_dev = (d(s.w1[0]), d(s.w1_sf[0]), d(s.w1_ws2), d(s.w2[0]), d(s.w2_sf[0]), d(s.w2_ws2))
+        log(f"generated and uploaded {cfg['E']} experts + shared in {time.time() - t0:.1f}s")
+
+
+def setup_moe(cfg, seed, stack=None):
     import numpy as np
     import torch
 
     from fp4_block_scaled_route_amd import ops, synth
 
-    t0 = time.time()
-    mi = synth.make_moe(cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"], seed=seed, routing=cfg["routing"],
-                        shared=cfg["shared"])
-    log(f"generated inputs in {time.time() - t0:.1f}s")
+    if stack is None or stack.key != (cfg["E"], cfg["H"], cfg["I"], seed):
+        stack = ExpertStack(cfg, seed)
+    x_host = synth.bf16_normal((cfg["T"], cfg["H"]), seed)
+    ids, w = synth.route(cfg["T"], cfg["E"], cfg["k"], seed, cfg["routing"])
+    mi = synth.MoEInputs(x=x_host, topk_ids=ids, topk_w=w, experts=stack.routed,
+                         shared=stack.shared if cfg["shared"] else None)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
-    ex = mi.experts
-    dev = dict(topk_ids=d(mi.topk_ids), topk_w=d(mi.topk_w), w1=d(ex.w1), w1_sf=d(ex.w1_sf),
-               w1_ws2=d(ex.w1_ws2), w2=d(ex.w2), w2_sf=d(ex.w2_sf), w2_ws2=d(ex.w2_ws2))
-    shared = None
-    if mi.shared is not None:
-        s = mi.shared
-        shared = (d(s.w1[0]), d(s.w1_sf[0]), d(s.w1_ws2), d(s.w2[0]), d(s.w2_sf[0]), d(s.w2_ws2))
+    dev = dict(topk_ids=d(mi.topk_ids), topk_w=d(mi.topk_w), **stack.dev)
+    shared = stack.shared_dev if cfg["shared"] else None
     x = mi.x.cuda()
     t, k, h, i, e = cfg["T"], cfg["k"], cfg["H"], cfg["I"], cfg["E"]
     ws = torch.empty(ops.moe_workspace_size(t, h, i, e, k, shared is not None, cfg["fp4"]),
                      dtype=torch.uint8, device="cuda")
     y = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
-    state = dict(mi=mi, dev=dev, shared=shared, x=x, ws=ws, y=y)
+    state = dict(mi=mi, dev=dev, shared=shared, x=x, ws=ws, y=y, stack=stack)
     if cfg["fp4"]:
         # warm-up calibration of the hidden activations' global scale (h kept
         # fp32 for this one call, a2_gs_out = max|h| / 2688)
@@ -169,10 +194,13 @@ def setup_moe(cfg, seed):
     return state
 
 
-def moe_step(cfg, st, events=None):
+def moe_step(cfg, st, events=None, quantize=True):
     from fp4_block_scaled_route_amd import ops
     if cfg["fp4"]:
-        xq, xs, gs = ops.quantize_act(st["x"], out=(st["xq"], st["xs"]), gs_out=st["gs"])
+        if quantize:
+            xq, xs, gs = ops.quantize_act(st["x"], out=(st["xq"], st["xs"]), gs_out=st["gs"])
+        else:
+            xq, xs, gs = st["xq"], st["xs"], st["gs"]
         return ops.moe_grouped(**st["dev"], x_fp4=xq, x_sf=xs, a1_gs=gs, shared=st["shared"], a2_gs=st["a2"],
                                workspace=st["ws"], out=st["y"], stage_events=events)
     return ops.moe_grouped(**st["dev"], x=st["x"], shared=st["shared"], workspace=st["ws"], out=st["y"],
@@ -182,9 +210,11 @@ def moe_step(cfg, st, events=None):
 SMALL_GROUP_ROWS = 4    # groups with more rows run on the LDS-staged kernel
 
 
-def moe_accounting(cfg, st):
+def moe_accounting(cfg, st, quantize=True):
     """Algorithmic FLOPs and bytes of one step and of the two gate/up GEMM
-    launches (groups of > 4 rows, the others), from the routing."""
+    launches (groups of > 4 rows, the others), from the routing.  Fully-FP4
+    step without the quantizer (quantize=False): the GEMMs read x_fp4 + scales
+    instead of bf16 x."""
     import numpy as np
     ids = st["mi"].topk_ids
     e, t, h, i, k = cfg["E"], cfg["T"], cfg["H"], cfg["I"], cfg["k"]
@@ -199,6 +229,8 @@ def moe_accounting(cfg, st):
     act_in = t * h * 2                                   # bf16 x (the fully-FP4 step quantizes it first)
     if cfg["fp4"]:
         act_in += t * (h // 2 + h // 16) * 2             # x_fp4 + scales written, then read by the GEMM
+        if not quantize:
+            act_in = t * (h // 2 + h // 16)              # x_fp4 + scales read by the GEMM
     out = t * h * 2
     w_bytes = (touched + S) * (BYTES_PER_EXPERT_W1 + BYTES_PER_EXPERT_W2)
     step_bytes = w_bytes + act_in + out
@@ -255,12 +287,18 @@ def moe_cpu_baseline(cfg, st, budget_s=12.0):
                 seconds=round(total_s, 2))
 
 
-def run_moe(args, cfg):
+MOE_NAMES = {"moe_decode": "MoE decode step", "moe_prefill": "MoE prefill chunk",
+             "moe_fp4": "fully FP4 MoE at large batch"}
+
+
+def time_moe(args, cfg, st, quantize=True):
+    """Warm-up, then args.steps timed steps: the step time (torch events
+    around all steps) and the dominant gate/up launch's time (HIP events the
+    library records around that one launch, on its stream)."""
     import torch
-    st = setup_moe(cfg, args.seed)
-    acc = moe_accounting(cfg, st)
+    acc = moe_accounting(cfg, st, quantize)
     for _ in range(args.warmup):
-        moe_step(cfg, st)
+        moe_step(cfg, st, quantize=quantize)
     torch.cuda.synchronize()
     hip = HipEvents()
     NEV = 8    # stage i runs from event i to event i + 1
@@ -283,23 +321,19 @@ def run_moe(args, cfg):
     t_wall = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        moe_step(cfg, st, events=timed_events(kev[s]))
+        moe_step(cfg, st, events=timed_events(kev[s]), quantize=quantize)
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(stop) / args.steps
     k_list = sorted(hip.elapsed_ms(e[0], e[1]) for e in kev)
-    k_ms = sum(k_list) / args.steps
-    k_med = k_list[len(k_list) // 2]
-    k_p90 = k_list[min(len(k_list) - 1, int(0.9 * len(k_list)))]
     for e in kev:
         hip.destroy(e)
     names = ["permute", "gate_up_big", "gate_up_small", "h_to_f16", "down_big", "down_small", "combine"]
     n_stage_steps = min(args.steps, 5)
     evs = [hip.create(NEV) for _ in range(n_stage_steps)]
     for s in range(n_stage_steps):
-        moe_step(cfg, st, events=evs[s])
+        moe_step(cfg, st, events=evs[s], quantize=quantize)
     torch.cuda.synchronize()
     stage = [0.0] * (NEV - 1)
     for s in range(n_stage_steps):
@@ -307,16 +341,20 @@ def run_moe(args, cfg):
             stage[i] += hip.elapsed_ms(evs[s][i], evs[s][i + 1]) / n_stage_steps
     for e in evs:
         hip.destroy(e)
-    src = kernel_source_hash()
-    gbs = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
-    tflops = acc["flops"] / (ms_step * 1e-3) / 1e12
+    return dict(acc=acc, part=part, ms_step=ms_step, t_wall=t_wall, k_ms=sum(k_list) / args.steps,
+                k_med=k_list[len(k_list) // 2], k_p90=k_list[min(len(k_list) - 1, int(0.9 * len(k_list)))],
+                stage={n: round(v, 4) for n, v in zip(names, stage)})
+
+
+def moe_roofline(args, cfg, tm, src):
+    acc, part, k_ms = tm["acc"], tm["part"], tm["k_ms"]
     kern = {"big": "nvfp4_gemm_lds (gate/up + SwiGLU, " +
                    ("all groups: > 16 rows per group on average)" if acc["large_batch"] else "groups of > 4 rows)"),
             "small": "nvfp4_gemm_compact (gate/up + SwiGLU, groups of <= 4 rows)"}[part]
     if cfg["fp4"]:
         kern = kern.replace("nvfp4_gemm_compact", "nvfp4_gemm_direct")
     kb, kf = acc["g1"][part]["bytes"], acc["g1"][part]["flops"]
-    traffic = read_traffic(args.workload, src)
+    traffic = read_traffic(cfg["name"], src)
     if cfg["fp4"]:
         ach = kf / (k_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=FP16_PEAK_TFLOPS, unit="TFLOP/s",
@@ -325,19 +363,28 @@ def run_moe(args, cfg):
         ach = kb / (k_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic)
-    roof.update(kernel=kern, kernel_ms=round(k_ms, 4), kernel_ms_median=round(k_med, 4), kernel_ms_p90=round(k_p90, 4),
-                groups=acc["g1"][part]["groups"],
+    roof.update(kernel=kern, kernel_ms=round(k_ms, 4), kernel_ms_median=round(tm["k_med"], 4),
+                kernel_ms_p90=round(tm["k_p90"], 4), groups=acc["g1"][part]["groups"],
                 algorithmic_bytes_per_launch=kb, algorithmic_flops_per_launch=kf)
+    return roof
+
+
+def run_moe(args, cfg, stack=None, cpu_budget_s=12.0):
+    """One MoE workload: the result line (and the state, for reuse)."""
+    st = setup_moe(cfg, args.seed, stack)
+    src = kernel_source_hash()
+    tm = time_moe(args, cfg, st)
+    acc, ms_step = tm["acc"], tm["ms_step"]
+    gbs = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
+    tflops = acc["flops"] / (ms_step * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
-        cpu = moe_cpu_baseline(cfg, st)
-    name = {"moe_decode": "MoE decode step", "moe_prefill": "MoE prefill chunk",
-            "moe_fp4": "fully FP4 MoE at large batch"}[args.workload]
+        log(f"timing the CPU oracle on a bounded sample of {cfg['name']} ...")
+        cpu = moe_cpu_baseline(cfg, st, budget_s=cpu_budget_s)
     result = {
         "metric": "NVFP4 MoE grouped-GEMM TFLOP/s + HBM GB/s (%roofline), 1xMI355X",
-        "value": round(gbs, 1),
-        "unit": "GB/s",
+        "value": round(tflops, 2) if cfg["fp4"] else round(gbs, 1),
+        "unit": "TFLOP/s" if cfg["fp4"] else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -347,24 +394,54 @@ def run_moe(args, cfg):
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{name}: {cfg['T']} tokens x hidden {cfg['H']}, {cfg['E']} experts top-{cfg['k']} "
-                               f"({cfg['routing']} routing), W1 [4096,7168] W2 [7168,2048] NVFP4"
+        "config": {"workload": f"{MOE_NAMES[cfg['name']]}: {cfg['T']} tokens x hidden {cfg['H']}, {cfg['E']} experts "
+                               f"top-{cfg['k']} ({cfg['routing']} routing), W1 [4096,7168] W2 [7168,2048] NVFP4"
                                f"{', shared expert' if cfg['shared'] else ''}"
-                               f"{', NVFP4 activations' if cfg['fp4'] else ', bf16 activations'}",
-                   "name": args.workload, "tokens": cfg["T"], "touched_experts": acc["touched"],
+                               f"{', NVFP4 activations (quantizer inside the step)' if cfg['fp4'] else ', bf16 activations'}",
+                   "name": cfg["name"], "tokens": cfg["T"], "touched_experts": acc["touched"],
                    "seed": args.seed, "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / FP16_PEAK_TFLOPS, 4),
+        "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": acc["step_bytes"],
         "algorithmic_flops_per_step": acc["flops"],
-        "stage_ms": {n: round(v, 4) for n, v in zip(names, stage)},
+        "stage_ms": tm["stage"],
         "stage_note": "per-stage times from separate steps with all stage events recorded",
-        "wall_s": round(t_wall, 4),
-        "roofline": roof,
+        "wall_s": round(tm["t_wall"], 4),
+        "roofline": moe_roofline(args, cfg, tm, src),
         "cpu_baseline": cpu,
         "kernel_source_hash": src,
     }
-    return result
+    if cfg["fp4"]:
+        # the same batch with x already quantized (only nvfp4_moe_grouped timed)
+        tq = time_moe(args, cfg, st, quantize=False)
+        fl = tq["acc"]["flops"] / (tq["ms_step"] * 1e-3) / 1e12
+        result["without_quantize"] = dict(
+            ms_per_step=round(tq["ms_step"], 4), tflops=round(fl, 2), mfma_frac=round(fl / FP16_PEAK_TFLOPS, 4),
+            hbm_gbs=round(tq["acc"]["step_bytes"] / (tq["ms_step"] * 1e-3) / 1e9, 1),
+            roofline=moe_roofline(args, cfg, tq, src), stage_ms=tq["stage"])
+    return result, st
+
+
+def run_headline(args):
+    """Default run: the fully-FP4 4096-token batch as the headline line, with
+    the decode and prefill steps nested; one expert stack for all three."""
+    import torch
+    stack = None
+    nested = {}
+    for name in ("moe_decode", "moe_prefill"):
+        res, st = run_moe(args, dict(WORKLOADS[name], name=name), stack, cpu_budget_s=8.0)
+        stack = st["stack"]
+        for key in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "data",
+                    "kernel_source_hash"):
+            res.pop(key, None)
+        nested[name] = res
+        del st
+        torch.cuda.synchronize()
+    head, _ = run_moe(args, dict(WORKLOADS["moe_fp4"], name="moe_fp4"), stack, cpu_budget_s=8.0)
+    head["configs"] = nested
+    return head
 
 
 # ---------------------------------------------------------------------------
@@ -692,7 +769,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="moe_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="headline", choices=["headline"] + sorted(WORKLOADS),
+                    help="headline (default): the fully-FP4 4096-token batch with the decode and prefill "
+                         "steps nested; or one workload")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -713,10 +792,16 @@ def main():
     if args.copy_calibration:
         run_copy(args)
         return
-    cfg = WORKLOADS[args.workload]
-    run = {"moe": run_moe, "linear": run_linear, "router": run_router,
-           "grouped_linear": run_grouped_linear, "rmsnorm_quant": run_rmsnorm_quant}[cfg["kind"]]
-    res = run(args, cfg)
+    if args.workload == "headline":
+        res = run_headline(args)
+    else:
+        cfg = dict(WORKLOADS[args.workload], name=args.workload)
+        if cfg["kind"] == "moe":
+            res, _ = run_moe(args, cfg)
+        else:
+            run = {"linear": run_linear, "router": run_router,
+                   "grouped_linear": run_grouped_linear, "rmsnorm_quant": run_rmsnorm_quant}[cfg["kind"]]
+            res = run(args, cfg)
     print(json.dumps(res), flush=True)
 
 
