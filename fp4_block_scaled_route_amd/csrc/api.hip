@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/nvfp4.h.
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/nvfp4.h"
 #include "nvfp4_internal.h"
@@ -114,6 +115,9 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_LAUNCH: return "a kernel launch failed";
     case NVFP4_ERR_ARG: return "incompatible combination of optional arguments";
+    case NVFP4_ERR_SCRATCH:
+      return "the call needs more scratch memory than nvfp4_moe_grouped_noalloc holds "
+             "(NVFP4_MOE_NOALLOC_SCRATCH_BYTES); use nvfp4_moe_grouped with a workspace";
     default: return "unknown status";
   }
 }
@@ -351,7 +355,37 @@ size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int6
   return moe_layout(T, H, I, E, topk, has_shared, h_fp4).total;
 }
 
-int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch memory of nvfp4_moe_grouped_noalloc: one array per GPU the
+// library runs on, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptr.
+__device__ __align__(256) uint8_t scratch[NVFP4_MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+// nvfp4_moe_grouped with the workspace taken from the caller's arguments
+// (noalloc == false) or from the scratch array (noalloc == true).
+int moe_grouped_impl(const nvfp4_moe_args* a, void* stream, bool noalloc) {
   if (!a) return NVFP4_ERR_NULL;
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, k = a->topk;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return NVFP4_ERR_SHAPE;
@@ -382,11 +416,19 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   for (const void* p : p4)
     if (p && !aligned(p, 4)) return NVFP4_ERR_ALIGN;
   const MoeLayout L = moe_layout(T, H, I, E, k, has_shared, h_fp4);
-  if (!a->workspace || a->workspace_bytes < L.total) return NVFP4_ERR_WORKSPACE;
-  if (!aligned(a->workspace, 256)) return NVFP4_ERR_ALIGN;
+  uint8_t* ws;
+  if (noalloc) {
+    if (a->workspace || a->workspace_bytes) return NVFP4_ERR_ARG;
+    if (L.total > NVFP4_MOE_NOALLOC_SCRATCH_BYTES) return NVFP4_ERR_SCRATCH;
+    ws = static_cast<uint8_t*>(scratch_for_current_device());
+    if (!ws) return NVFP4_ERR_LAUNCH;
+  } else {
+    if (!a->workspace || a->workspace_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(a->workspace, 256)) return NVFP4_ERR_ALIGN;
+    ws = static_cast<uint8_t*>(a->workspace);
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   int* offsets = reinterpret_cast<int*>(ws + L.offsets);
   int* glist = reinterpret_cast<int*>(ws + L.glist);
   int* gcount = reinterpret_cast<int*>(ws + L.gcount);
@@ -562,5 +604,13 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
   ev(7);
   return NVFP4_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) { return moe_grouped_impl(a, stream, false); }
+
+int nvfp4_moe_grouped_noalloc(const nvfp4_moe_args* a, void* stream) { return moe_grouped_impl(a, stream, true); }
 
 }  // extern "C"

@@ -31,6 +31,7 @@ EXPORTED = (
     "nvfp4_grouped_linear",
     "nvfp4_moe_workspace_size",
     "nvfp4_moe_grouped",
+    "nvfp4_moe_grouped_noalloc",
     "nvfp4_router_prepare",
     "nvfp4_router_workspace_size",
     "nvfp4_router_topk",
@@ -157,6 +158,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_workspace_size.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
         L.nvfp4_moe_grouped.restype = ctypes.c_int
         L.nvfp4_moe_grouped.argtypes = [ctypes.POINTER(MoeArgs), _c_ptr]
+        L.nvfp4_moe_grouped_noalloc.restype = ctypes.c_int
+        L.nvfp4_moe_grouped_noalloc.argtypes = [ctypes.POINTER(MoeArgs), _c_ptr]
         L.nvfp4_router_prepare.restype = ctypes.c_int
         L.nvfp4_router_prepare.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]
         L.nvfp4_router_workspace_size.restype = ctypes.c_size_t
@@ -362,20 +365,31 @@ def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
                 a2_gs: Optional[torch.Tensor] = None, a2_gs_out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None,
                 offsets_out: Optional[torch.Tensor] = None, perm_out: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None, stage_events: Optional[Sequence[int]] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, stage_events: Optional[Sequence[int]] = None,
+                noalloc: bool = False) -> torch.Tensor:
     """One MoE layer (see nvfp4_moe_grouped in include/nvfp4.h).
-    ``shared`` = (s1, s1_sf, s1_ws2, s2, s2_sf, s2_ws2) or None."""
+    ``shared`` = (s1, s1_sf, s1_ws2, s2, s2_sf, s2_ws2) or None.
+    ``noalloc``: call nvfp4_moe_grouped_noalloc instead (no workspace; the
+    library's static scratch array; ``out`` must then be given too, so that
+    nothing is allocated)."""
     (t, h, i, e, topk), specs = _moe_specs(topk_ids, topk_w, w1, w1_sf, w1_ws2, w2, w2_sf, w2_ws2, x, x_fp4, x_sf,
                                            a1_gs, shared, a2_gs, a2_gs_out, workspace, offsets_out, perm_out, out)
     dev = _validate(specs)
-    need = moe_workspace_size(t, h, i, e, topk, shared is not None, a2_gs is not None)
-    if workspace is not None and workspace.numel() < need:
-        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
     if stage_events is not None and len(stage_events) != 8:
         raise ValueError("stage_events must hold 8 hipEvent_t handles (0 to skip one)")
-    y = out if out is not None else torch.empty((t, h), dtype=torch.bfloat16, device=dev)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc calls take no workspace")
+        if out is None:
+            raise ValueError("noalloc calls need `out` (nothing is allocated)")
+        y = out
+    else:
+        need = moe_workspace_size(t, h, i, e, topk, shared is not None, a2_gs is not None)
+        if workspace is not None and workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+        y = out if out is not None else torch.empty((t, h), dtype=torch.bfloat16, device=dev)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     a = MoeArgs()
     a.T, a.H, a.I, a.E, a.topk = t, h, i, e, topk
     a.x, a.x_fp4, a.x_sf, a.a1_gs = _p(x), _p(x_fp4), _p(x_sf), _p(a1_gs)
@@ -388,13 +402,14 @@ def moe_grouped(topk_ids: torch.Tensor, topk_w: torch.Tensor,
         a.s1, a.s1_sf, a.s1_ws2 = _p(s1), _p(s1_sf), _p(s1_ws2)
         a.s2, a.s2_sf, a.s2_ws2 = _p(s2), _p(s2_sf), _p(s2_ws2)
     a.workspace = _p(workspace)
-    a.workspace_bytes = workspace.numel()
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
     a.offsets_out, a.perm_out = _p(offsets_out), _p(perm_out)
     a.y = _p(y)
     if stage_events is not None:
         arr = (_c_ptr * len(stage_events))(*[_c_ptr(int(v)) for v in stage_events])
         a.stage_events = ctypes.cast(arr, ctypes.POINTER(_c_ptr))
-    _check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream(dev)))
+    fn = lib().nvfp4_moe_grouped_noalloc if noalloc else lib().nvfp4_moe_grouped
+    _check(fn(ctypes.byref(a), _stream(dev)))
     return y
 
 

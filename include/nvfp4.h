@@ -62,7 +62,8 @@ enum {
   NVFP4_ERR_ALIGN = -3,     /* a pointer is not aligned as required */
   NVFP4_ERR_WORKSPACE = -4, /* workspace missing or smaller than the size function says */
   NVFP4_ERR_LAUNCH = -5,    /* a kernel launch failed (hipGetLastError) */
-  NVFP4_ERR_ARG = -6        /* an incompatible combination of optional arguments */
+  NVFP4_ERR_ARG = -6,       /* an incompatible combination of optional arguments */
+  NVFP4_ERR_SCRATCH = -7    /* nvfp4_moe_grouped_noalloc: the call needs more scratch than it holds */
 };
 
 /* Host: a static, human-readable description of a status code. */
@@ -247,6 +248,31 @@ typedef struct nvfp4_moe_args {
 size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                                 int has_shared, int h_fp4);
 int nvfp4_moe_grouped(const nvfp4_moe_args* args, void* stream);
+
+/*
+ * nvfp4_moe_grouped_noalloc - nvfp4_moe_grouped for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, same kernels and the
+ * same results, but args->workspace must be NULL and args->workspace_bytes 0
+ * (NVFP4_ERR_ARG otherwise): the scratch memory comes from a static device
+ * array of NVFP4_MOE_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  Nothing is allocated or freed.
+ *   Capacity: a call whose nvfp4_moe_workspace_size(...) exceeds
+ *   NVFP4_MOE_NOALLOC_SCRATCH_BYTES returns NVFP4_ERR_SCRATCH before any
+ *   launch.  At hidden 7168, intermediate 2048, 384 experts, top-8 that is
+ *   any batch of at most 297 tokens with a shared expert and bf16 h, or 545
+ *   tokens with NVFP4 h and no shared expert (the 64-token decode step
+ *   needs 51.6 MiB, the 128-token prefill chunk 31 MiB).
+ *   Device: the array of the current device is used (its address is looked
+ *   up on the first call on each device); `stream` must belong to it.
+ *   Concurrency: every call on one GPU shares that GPU's array, which keeps
+ *   the last call's contents (every call initialises what it reads).  Calls
+ *   that overlap in time on one GPU (on different streams, or from
+ *   different threads without ordering) race on it: order them on one
+ *   stream.  The caller still owns and passes all inputs and outputs.
+ */
+#define NVFP4_MOE_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+int nvfp4_moe_grouped_noalloc(const nvfp4_moe_args* args, void* stream);
 
 /*
  * Router gate (page "commit 1121cd7 - single_shot_inference.py", note on the

@@ -36,8 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.nvfp4_abi_version() == ops.ABI_VERSION
-    for code in (0, -1, -2, -3, -4, -5, -6):
-        assert lib.nvfp4_status_string(code)
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert lib.nvfp4_status_string(code) != b"unknown status"
     assert lib.nvfp4_status_string(-99) == b"unknown status"
 
 
@@ -149,6 +149,31 @@ def test_moe_validation(lib):
     assert base(a2_gs=FAKE, a2_gs_out=FAKE) == -6
     assert base(workspace_bytes=ws - 1) == -4
     assert base(y=ctypes.c_void_p(0x1008)) == -3
+
+
+def test_moe_noalloc_validation(lib):
+    """Host-side checks of the no-allocation entry point: the same argument
+    checks as nvfp4_moe_grouped, no workspace accepted, and calls needing
+    more than the static scratch array rejected before any launch."""
+    L = lib
+
+    def call(**kw):
+        a = ops.MoeArgs()
+        a.T, a.H, a.I, a.E, a.topk = 64, 7168, 2048, 384, 8
+        for f in ("x", "topk_ids", "topk_w", "w1", "w1_sf", "w1_ws2", "w2", "w2_sf", "w2_ws2", "y"):
+            setattr(a, f, FAKE)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return L.nvfp4_moe_grouped_noalloc(ctypes.byref(a), None)
+    assert call(T=0) == 0
+    assert call(H=7000) == -2
+    assert call(w1=None) == -1
+    assert call(workspace=FAKE, workspace_bytes=1 << 30) == -6    # no workspace is taken
+    limit = 72 << 20
+    assert L.nvfp4_moe_workspace_size(298, 7168, 2048, 384, 8, 1, 0) > limit
+    assert L.nvfp4_moe_workspace_size(297, 7168, 2048, 384, 8, 1, 0) <= limit
+    assert call(T=298, s1=FAKE, s1_sf=FAKE, s1_ws2=FAKE, s2=FAKE, s2_sf=FAKE, s2_ws2=FAKE) == -7
+    assert call(T=4096, x=None, x_fp4=FAKE, x_sf=FAKE, a1_gs=FAKE, a2_gs=FAKE) == -7
 
 
 def test_router_validation(lib):
