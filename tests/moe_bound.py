@@ -28,14 +28,25 @@ GPU arithmetic, in order (bf16 activations unless noted):
 
 Bounds used.  Rounding to bf16 (8 significant bits) has relative error at most
 u_bf16 = 2^-8 and is bounded deterministically.  Accumulation errors of the
-fp32 sums use the probabilistic bound of Higham and Mary ("A new approach to
-probabilistic rounding error analysis", SIAM J. Sci. Comput. 2019):
-|error| <= lam * sqrt(n) * u * sum|terms|, which fails with probability at
-most 2 exp(-lam^2 / 2) per sum under their model of independent rounding
-errors (lam = 7: below 5e-11).  The effect of the element errors of h on a
+fp32 sums follow the probabilistic model of Higham and Mary ("A new approach
+to probabilistic rounding error analysis", SIAM J. Sci. Comput. 2019): the n
+rounding errors delta_i are independent, zero-mean and at most u in size, so
+the error sum_i delta_i s_i (s_i the partial sums) stays below
+lam * u * sqrt(sum_i s_i^2) except with probability 2 exp(-lam^2 / 2)
+(lam = 7: below 5e-11).  For the zero-mean synthetic operands here the
+partial sums behave like a random walk over the terms t_i, whose
+sum_i s_i^2 is at most about n * sum_i t_i^2, so the bound used is
+lam * u * sqrt(n) * ||t||_2.  (Their worst-case form with sum|t_i| in place
+of sqrt(n) * ||t||_2, about sqrt(n) = 85 times looser at K = 7168, leaves h
+so uncertain that 16% of the fully-FP4 path's block scales could flip, and the
+bound then checks nothing.)  The effect of the element errors of h on a
 down-GEMM output is bounded the same way, by Hoeffding's inequality over the
-I independent terms: lam * sqrt(sum_k (dh_k * W2[n, k])^2).  Code and scale
-flips of the fully-FP4 path are added deterministically (L1).  The bound is
+I independent terms: lam * sqrt(sum_k (dh_k * W2[n, k])^2).  Code flips of
+the fully-FP4 path (GPU and oracle on opposite sides of a rounding midpoint)
+enter that sum as independent terms of random sign; a scale-byte flip moves
+its 16-element block as one term.  Where the plain sum of the term bounds is
+smaller than lam times their 2-norm (few terms), that deterministic sum is
+used instead.  The bound is
 therefore a high-probability bound under that model, not a worst case: the
 worst case over every rounding in a 7168-term sum (n * u * sum|terms|) is
 looser than the output values themselves and would check nothing.
@@ -57,7 +68,8 @@ LAM = 7.0
 
 
 def _acc(n):
-    """Probabilistic accumulation factor for an n-term fp32 sum."""
+    """Probabilistic accumulation factor for an n-term fp32 sum (times the
+    2-norm of its terms)."""
     return LAM * np.sqrt(n) * U32
 
 
@@ -85,15 +97,16 @@ class MoeBound:
         g, u = gu[:, :i_dim], gu[:, i_dim:]
         aa = np.abs(a)
         # 1-2: accumulation, scale products, fp16 staging of x.  One pass over
-        # |W1| (float32 is ample for a bound) gives sum_m |a_m W1[k, m]| for
-        # every row and, in its last row, sum_m |W1[k, m]|.
-        aw1 = np.absolute(w1d, dtype=np.float32)
-        ext = np.vstack([aa, np.ones((1, h_dim))]).astype(np.float32)
-        sums = (ext @ aw1.T).astype(np.float64)
-        del aw1
-        egu = _acc(h_dim) * sums[:-1] + 3 * U32 * np.abs(gu)
+        # W1^2 (float32 is ample for a bound) gives sum_m (a_m W1[k, m])^2 for
+        # every row and, in its last row, sum_m W1[k, m]^2.
+        sw1 = np.square(w1d, dtype=np.float32)
+        ext = np.vstack([aa * aa, np.ones((1, h_dim))]).astype(np.float32)
+        sums = (ext @ sw1.T).astype(np.float64)
+        del sw1
+        egu = _acc(h_dim) * np.sqrt(sums[:-1]) + 3 * U32 * np.abs(gu)
         if not self.x_fp4:
-            egu += SUB * aa.max(axis=1, keepdims=True) * sums[-1][None, :]
+            # sum_m |W1[k, m]| <= sqrt(H) * ||W1[k]||_2
+            egu += SUB * aa.max(axis=1, keepdims=True) * np.sqrt(h_dim * sums[-1])[None, :]
         eg, eu = egu[:, :i_dim], egu[:, i_dim:]
         # 3: SwiGLU in fp32 (|silu'| <= 1.1)
         sg = moe.silu(g)
@@ -106,12 +119,26 @@ class MoeBound:
             # 4-5: fp16 h, then the down GEMM
             hmax = (np.abs(h) + eh).max(axis=1, keepdims=True)
             dh = U16 * (np.abs(h) + eh) + eh + SUB * hmax
-            e_lin = LAM * np.sqrt((f32(dh * dh) @ np.square(aw2).T).astype(np.float64))
-            e_acc = _acc(i_dim) * (f32(np.abs(h) + dh) @ aw2.T)
+            e_lin = np.minimum(LAM * np.sqrt((f32(dh * dh) @ np.square(aw2).T).astype(np.float64)),
+                               (f32(dh) @ aw2.T).astype(np.float64))
+            e_acc = _acc(i_dim) * np.sqrt((f32(np.square(np.abs(h) + dh)) @ np.square(aw2).T).astype(np.float64))
         else:
-            hq, dh = self._fp4_hidden(h, eh)
-            e_lin = (f32(dh) @ aw2.T).astype(np.float64)
-            e_acc = _acc(i_dim) * (f32(np.abs(hq) + dh) @ aw2.T)
+            hq, dh, blocks = self._fp4_hidden(h, eh)
+            # a code flip moves one element up or down with the sign of the
+            # GPU's rounding error of h: independent, zero-mean terms
+            # (Hoeffding, like the fp16 rounding above); a scale-byte flip
+            # moves its whole 16-element block together, so a block's effect
+            # is summed first and the blocks then enter Hoeffding's sum
+            e2 = (f32(dh * dh) @ np.square(aw2).T).astype(np.float64)
+            e1 = (f32(dh) @ aw2.T).astype(np.float64)
+            for (row, b, d16) in blocks:
+                tb = (aw2[:, 16 * b:16 * b + 16] @ d16.astype(np.float32)).astype(np.float64)
+                e2[row] += tb * tb
+                e1[row] += tb
+            # with few terms the plain sum is the tighter of the two bounds
+            e_lin = np.minimum(LAM * np.sqrt(e2), e1)
+            e_acc = _acc(i_dim) * np.sqrt(
+                (f32(np.square(np.abs(hq) + dh + self._blk_dense(blocks, hq.shape))) @ np.square(aw2).T).astype(np.float64))
         # float32 sums of non-negative terms: relative error below 1e-3 at
         # these lengths, covered by the 1.01 factor
         e_lin = 1.01 * e_lin
@@ -155,13 +182,23 @@ class MoeBound:
         val = codec.E2M1_VALUES
         jump = np.abs(val[c_hi] - val[c_lo]) * np.repeat(scale, 16, axis=1)
         jump = np.where(c_lo == c_hi, 0.0, np.maximum(jump, 0.0))
-        # scale byte flips: the element may be quantized under either scale
+        # scale byte flips: every element of the block may be quantized under
+        # either scale (up to twice the coarser step, plus the h error)
         unstable = np.repeat(~byte_stable, 16, axis=1)
         big = 2.0 * np.repeat(np.maximum(s_lo, s_hi), 16, axis=1) + et
-        dh = np.where(unstable, big, jump)
+        dh = np.where(unstable, 0.0, jump)
+        blocks = [(int(r_), int(b_), big[r_, 16 * b_:16 * b_ + 16])
+                  for r_, b_ in zip(*np.nonzero(~byte_stable))]
         with self.lock:
-            self.flips += int(np.count_nonzero(dh))
-        return hq, dh
+            self.flips += int(np.count_nonzero(dh)) + 16 * len(blocks)
+        return hq, dh, blocks
+
+    @staticmethod
+    def _blk_dense(blocks, shape):
+        d = np.zeros(shape)
+        for (row, b, d16) in blocks:
+            d[row, 16 * b:16 * b + 16] = d16
+        return d
 
     # -- whole layer --------------------------------------------------------
 
@@ -221,8 +258,8 @@ def linear_reference_and_bound(x_rows, w_packed, w_sf, ws2, x_fp4=False):
     ref = linear.linear_bf16(x, w_packed, w_sf, ws2)
     awd = np.abs(codec.dequant_nvfp4(w_packed, w_sf, ws2))
     k = x.shape[1]
-    sums = np.abs(x) @ awd.T
-    e = (_acc(k + 16) + 3 * U32) * sums + 3 * U32 * np.abs(ref)
+    norm2 = np.sqrt((x * x) @ (awd * awd).T)
+    e = _acc(k + 16) * norm2 + 3 * U32 * (np.abs(x) @ awd.T) + 3 * U32 * np.abs(ref)
     if not x_fp4:
         e += SUB * np.abs(x).max(axis=1, keepdims=True) * awd.sum(axis=1)[None, :]
     e *= 1.01
