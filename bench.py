@@ -444,6 +444,53 @@ def run_headline(args):
     return head
 
 
+def time_graph(call, n_calls, reps=5):
+    """ms per call of n_calls back-to-back calls captured in one graph and
+    replayed reps times: the GPU time of a call with its launches issued
+    back to back, without the host work of the Python binding in between
+    (which exceeds the GPU time of a microsecond-scale call).  call(i) must
+    read the current stream when it runs."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (reps * n_calls)
+    del g
+    return ms
+
+
+def time_eager(call, warmup, steps):
+    """ms per call of steps calls issued from Python (host work included)."""
+    import torch
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
 # ---------------------------------------------------------------------------
 # dense linear workload
 # ---------------------------------------------------------------------------
@@ -465,18 +512,16 @@ def run_linear(args, cfg):
     ws2 = torch.tensor([li.ws2], dtype=torch.float32, device="cuda")
     x = li.x.cuda()
     y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    work = torch.empty(max(1, ops.lib().nvfp4_linear_workspace_size(m, n, k)), dtype=torch.uint8, device="cuda")
-    for i in range(args.warmup):
+    need = ops.lib().nvfp4_linear_workspace_size(m, n, k)
+    work = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+
+    def call(i):
         ops.linear(ws[i % copies], sfs[i % copies], ws2, x=x, out=y, workspace=work)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        ops.linear(ws[i % copies], sfs[i % copies], ws2, x=x, out=y, workspace=work)
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms_eager = time_eager(call, args.warmup, args.steps)
+    y_eager = y.clone()
+    ms = time_graph(call, args.steps)
+    if not torch.equal(y, y_eager):
+        raise RuntimeError("graph replay of the linear differs from the eager call")
     nbytes = w_bytes + m * k * 2 + m * n * 2
     flops = 2 * m * n * k
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -505,7 +550,9 @@ def run_linear(args, cfg):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"dense NVFP4 linear x[{m},{k}] @ W[{n},{k}]^T, bf16 out, {copies} rotating "
-                               f"weight copies", "name": args.workload},
+                               f"weight copies", "name": args.workload,
+                   "timing": f"{args.steps} back-to-back calls captured in one graph, replayed 5 times"},
+        "eager_ms_per_call": round(ms_eager, 5), "workspace_bytes": need,
         "tflops": round(flops / (ms * 1e-3) / 1e12, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None),
@@ -533,17 +580,10 @@ def run_router(args, cfg):
     ids = torch.empty((t, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((t, k), dtype=torch.float32, device="cuda")
     work = torch.empty(max(1, ops.router_workspace_size(t, h, e)), dtype=torch.uint8, device="cuda")
-    for i in range(args.warmup):
+    def call(i):
         ops.router_topk(x, wrs[i % copies], k, logits, ids, wts, work)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        ops.router_topk(x, wrs[i % copies], k, logits, ids, wts, work)
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms_eager = time_eager(call, args.warmup, args.steps)
+    ms = time_graph(call, args.steps)
     # algorithmic: weight + activations read, logits written, selection written
     nbytes = w_bytes + t * h * 2 + t * e * 4 + t * k * 8
     flops = 2 * t * e * h
@@ -584,7 +624,9 @@ def run_router(args, cfg):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"router gate: {t} tokens x hidden {h}, {e} experts, top-{k} softmax, FP8 "
                                f"round-tripped bf16 weight, {copies} rotating weight copies",
-                   "name": args.workload},
+                   "name": args.workload,
+                   "timing": f"{args.steps} back-to-back calls captured in one graph, replayed 5 times"},
+        "eager_ms_per_call": round(ms_eager, 5),
         "tflops": round(tfl, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": roof, "cpu_baseline": cpu,
     }
@@ -608,19 +650,14 @@ def run_grouped_linear(args, cfg):
     ws2 = torch.from_numpy(gi.ws2).cuda()
     xs = [x.clone() for _ in range(min(copies, 8))]
     y = torch.empty((t, g, n), dtype=torch.bfloat16, device="cuda")
-    work = torch.empty(max(1, ops.grouped_linear_workspace_size(t, g, n, k)), dtype=torch.uint8, device="cuda")
+    need = ops.grouped_linear_workspace_size(t, g, n, k)
+    work = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     nw, nx = len(ws), len(xs)
-    for i in range(args.warmup):
+
+    def call(i):
         ops.grouped_linear(*ws[i % nw], ws2, x=xs[i % nx], out=y, workspace=work)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        ops.grouped_linear(*ws[i % nw], ws2, x=xs[i % nx], out=y, workspace=work)
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms_eager = time_eager(call, args.warmup, args.steps)
+    ms = time_graph(call, args.steps)
     nbytes = w_bytes + t * g * k * 2 + t * g * n * 2
     flops = 2 * t * g * n * k
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -632,7 +669,8 @@ def run_grouped_linear(args, cfg):
     else:
         roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
-    roof.update(kernel="nvfp4_rows_to_f16 + grouped GEMM (one call)", kernel_ms=round(ms, 5),
+    roof.update(kernel="grouped GEMM (one call: one launch up to 4 tokens, else fp16 staging + GEMM)",
+                kernel_ms=round(ms, 5),
                 algorithmic_bytes_per_launch=nbytes, algorithmic_flops_per_launch=flops)
     cpu = None
     if not args.no_cpu_baseline:
@@ -659,7 +697,9 @@ def run_grouped_linear(args, cfg):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"grouped linear wo_a: {t} tokens x {g} groups, K {k} per group, width {n}, "
                                f"NVFP4 weights, bf16 activations, {nw} rotating weight copies",
-                   "name": args.workload},
+                   "name": args.workload,
+                   "timing": f"{args.steps} back-to-back calls captured in one graph, replayed 5 times"},
+        "eager_ms_per_call": round(ms_eager, 5),
         "tflops": round(tfl, 3), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": roof, "cpu_baseline": cpu,
     }
@@ -684,34 +724,24 @@ def run_rmsnorm_quant(args, cfg):
     y = torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
     work = torch.empty(max(16, ops.lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8, device="cuda")
     L = ops.lib()
-    s = torch.cuda.current_stream().cuda_stream
 
     def fused(i):
+        s = torch.cuda.current_stream().cuda_stream
         ops._check(L.nvfp4_rmsnorm_quantize(xs[i % copies].data_ptr(), w.data_ptr(), eps, t, k, None,
                                             gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), work.data_ptr(),
                                             work.numel(), s))
 
     def unfused(i):
+        s = torch.cuda.current_stream().cuda_stream
         ops._check(L.nvfp4_rmsnorm_quantize(xs[i % copies].data_ptr(), w.data_ptr(), eps, t, k, y.data_ptr(),
                                             gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), work.data_ptr(),
                                             work.numel(), s))
         ops._check(L.nvfp4_quantize_act(y.data_ptr(), t, k, gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), s))
 
-    def timed(fn):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for i in range(args.steps):
-            fn(i)
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps
-
-    ms = timed(fused)
-    ms_unfused = timed(unfused)
+    ms_eager = time_eager(fused, args.warmup, args.steps)
+    ms = time_graph(fused, args.steps)
+    time_eager(unfused, args.warmup, 1)
+    ms_unfused = time_graph(unfused, args.steps)
     nbytes = t * k * 2 + k * 2 + t * (k // 2) + t * (k // 16) + 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     cpu = None
@@ -739,8 +769,9 @@ def run_rmsnorm_quant(args, cfg):
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"RMSNorm of x [{t}, {k}] bf16 with a bf16 weight, fused with the NVFP4 quantizer "
-                               f"(global scale computed), {copies} rotating inputs", "name": args.workload},
-        "unfused_ms": round(ms_unfused, 5),
+                               f"(global scale computed), {copies} rotating inputs", "name": args.workload,
+                   "timing": f"{args.steps} back-to-back calls captured in one graph, replayed 5 times"},
+        "eager_ms_per_call": round(ms_eager, 5), "unfused_ms": round(ms_unfused, 5),
         "roofline": dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
                          kernel="nvfp4_rmsnorm_stats + nvfp4_rmsnorm_quant (one call)", kernel_ms=round(ms, 5),

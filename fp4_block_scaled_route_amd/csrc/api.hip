@@ -223,15 +223,18 @@ size_t staging_bytes(int64_t rows, int64_t K) {
   return round_up(sizeof(int32_t) * (size_t)rows, 256) + round_up(sizeof(uint16_t) * (size_t)rows * K, 256);
 }
 
+// Bytes one call needs (0 on the skinny kernel, which stages in LDS).
+size_t gl_need(int64_t T, int64_t G, int64_t N, int64_t K, bool fp4) {
+  if (skinny_plan(T, G, N, K, fp4).ok) return 0;
+  const GlPlan p = gl_plan(T, G, N, K, fp4);
+  size_t need = fp4 ? 0 : staging_bytes(T * G, K);
+  if (p.ksplit > 1) need = staging_bytes(T * G, K) + round_up(sizeof(float) * (size_t)p.ksplit * T * G * N, 256);
+  return need;
+}
+
 size_t gl_workspace(int64_t T, int64_t G, int64_t N, int64_t K) {
   if (T <= 0 || G <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || T * G >= kMaxDim) return 0;
-  size_t worst = staging_bytes(T * G, K);
-  for (int fp4 = 0; fp4 < 2; ++fp4) {
-    const GlPlan p = gl_plan(T, G, N, K, fp4 != 0);
-    if (p.ksplit > 1)
-      worst = std::max(worst, staging_bytes(T * G, K) + round_up(sizeof(float) * (size_t)p.ksplit * T * G * N, 256));
-  }
-  return worst;
+  return std::max(gl_need(T, G, N, K, false), gl_need(T, G, N, K, true));
 }
 
 // The dense linear (G = 1) and the grouped linear: validation, then the launches.
@@ -253,12 +256,36 @@ int gl_run(const void* x_bf16, const uint8_t* x_fp4, const uint8_t* x_sf, const 
   if (fp4 && (!aligned(x_fp4, 16) || !aligned(x_sf, 16) || !aligned(gsa, 4))) return NVFP4_ERR_ALIGN;
   if (!fp4 && !aligned(x_bf16, 16)) return NVFP4_ERR_ALIGN;
   const int64_t rows = T * G;   // activation rows of K: row t * G + g
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const SkinnyPlan sk = skinny_plan(T, G, N, K, fp4);
+  if (sk.ok) {
+    // one launch, no workspace
+    GemmArgs g{};
+    g.w = w_fp4;
+    g.w_sf = w_sf;
+    g.w_ws2 = ws2;
+    g.w_gstride = N * (K / 2);
+    g.sf_gstride = N * (K / 16);
+    g.n_routed = (int)G;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.a = fp4 ? static_cast<const void*>(x_fp4) : x_bf16;
+    g.a_rows = (int)rows;
+    g.a_sf = x_sf;
+    g.gsa = fp4 ? gsa : nullptr;
+    g.y = static_cast<uint16_t*>(y_bf16);
+    g.gl_T = (int)T;
+    g.gl_G = (int)G;
+    g.nb = sk.nb;
+    g.sk_kp = sk.kp;
+    g.sk_u = sk.u;
+    return launch_status(launch_gemm_skinny(g, fp4 ? A_FP4 : A_F16, sk, s));
+  }
   const GlPlan plan = gl_plan(T, G, N, K, fp4);
   if (!fp4 || plan.ksplit > 1) {
     if (!workspace || workspace_bytes < gl_workspace(T, G, N, K)) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* wsp = static_cast<uint8_t*>(workspace);
   int* rowshift = reinterpret_cast<int*>(wsp);
   f16* x16 = fp4 ? nullptr : reinterpret_cast<f16*>(wsp + round_up(sizeof(int32_t) * (size_t)rows, 256));

@@ -40,6 +40,8 @@
 // [16*MAXC rows, 256] into LDS (double buffered) and every wave reads its B
 // fragments from there, so the activation rows are fetched once per
 // workgroup instead of once per wave.
+#include <algorithm>
+
 #include "device_util.h"
 
 namespace nvfp4 {
@@ -1021,6 +1023,247 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// skinny kernel: at most 4 activation rows per group, one launch per call
+// ---------------------------------------------------------------------------
+//
+// The dense and grouped linear at decode sizes read a few MB to tens of MB of
+// weights once, so a call is one pass of the memory system plus launch
+// costs.  A compute unit keeps only so many loads in flight and a memory
+// round trip under load takes microseconds, so every wave requests its
+// whole share at once and computes chunk by chunk as the data arrives.
+//  * Work item (workgroup) = (group, R fragments of 16 weight rows); its
+//    sk_kp <= 16 waves split K into ranges of U <= 4 chunks (the last may
+//    be shorter), as short as the waves and the LDS allow.
+//  * Each activation chunk of the group's T <= 4 rows is converted in the
+//    wave's own LDS slots, so no wave waits for another until the end: bf16
+//    rows are scaled by the power of two that takes the row's maximum over
+//    the chunk into [2^14, 2^15) (exact for values within 29 binades of it);
+//    the chunk's MFMA sums start from zero and are added to the fp32 total
+//    with that power of two undone (exact scaling, one fp32 addition per
+//    chunk).  NVFP4 rows are decoded exactly (no shift).
+//  * The range totals of a fragment meet in LDS and are added in range
+//    order; the global scales multiply the sum.
+constexpr int kSkinnyRows = 4;
+constexpr int kSkinnyMaxWaves = 16;
+constexpr int kSkinnyLds = 64 * 1024;
+constexpr int kSkinnyPitch = kChunk * 2 + 64;   // LDS bytes per staged row of a chunk (rows 16 banks apart)
+
+// Max over each 16-lane row of the wave; every lane gets its row's max.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  return v;
+}
+
+template <int R>
+struct SkW {
+  u32x4 h0[R], h1[R];   // codes of a chunk, whole rows (rows 0-7, 8-15 of the fragment)
+  uint32_t s[R];        // this lane's scale word of the chunk
+};
+
+template <int R, int U, int AM>
+__global__ __launch_bounds__(kSkinnyMaxWaves * 64) void nvfp4_gemm_skinny(const GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sk[];
+  const int lane = threadIdx.x & 63;
+  const int kp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // this wave's range
+  const int lr = lane & 15, lg = lane >> 4;
+  const int KP = a.sk_kp;
+  const int g = blockIdx.x / a.nb, nbk = blockIdx.x - g * a.nb;
+  const int G = a.gl_G, T = a.gl_T;   // activation and output row of token t: t * G + g
+  const int K = a.K, nkc = K / kChunk;
+  const int c0 = kp * U;
+  const int cnt = min(U, nkc - c0);   // >= 1 by the plan
+
+  // weights
+  const uint32_t KB = K / 2, KS = K / 16;
+  const rsrc_t rw = make_rsrc(a.w + (int64_t)g * a.w_gstride, (uint32_t)a.N * KB);
+  const rsrc_t rs = make_rsrc(a.w_sf + (int64_t)g * a.sf_gstride, (uint32_t)a.N * KS);
+  const uint32_t vrow = (lane & 7) * KB + (lane >> 3) * 16;   // whole-row code loads
+  const uint32_t vs = lr * KS + lg * 4;
+  int fbase[R];
+  bool fvalid[R];
+  uint32_t sw[R], ss[R];
+#pragma unroll
+  for (int f = 0; f < R; ++f) {
+    fbase[f] = (nbk * R + f) * 16;
+    fvalid[f] = fbase[f] < a.N;
+    const uint32_t row0 = fvalid[f] ? (uint32_t)fbase[f] : 0u;
+    sw[f] = row0 * KB;
+    ss[f] = row0 * KS;
+  }
+
+  // activations: bf16 x0 = rows 0, 1 (lanes 0-31, 32-63; 8 values at column
+  // 8 * (lane % 32)), x1 = rows 2, 3 (requested only when T > 2).  NVFP4:
+  // x0 = codes (lanes 0-31: row lane / 8, 32 codes at 32 * (lane % 8)), x1[0]
+  // = scales (lanes 32-47: row (lane - 32) / 4, blocks 4 * (lane % 4) ..).
+  // Rows past T: no memory access, zeros.
+  const uint32_t rowb = AM == A_F16 ? K * 2 : K / 2;
+  const rsrc_t rx = make_rsrc(a.a, (uint32_t)a.a_rows * rowb);
+  const rsrc_t rxs = make_rsrc(a.a_sf, AM == A_F16 ? 0u : (uint32_t)a.a_rows * KS);
+  uint32_t vx0, vx1;
+  if constexpr (AM == A_F16) {
+    const int r0 = lane >> 5, r1 = r0 + 2;
+    vx0 = r0 < T ? (uint32_t)(r0 * G + g) * rowb + (lane & 31) * 16 : kPast;
+    vx1 = r1 < T ? (uint32_t)(r1 * G + g) * rowb + (lane & 31) * 16 : kPast;
+  } else {
+    const int rq = lane >> 3, rsr = (lane - 32) >> 2;
+    vx0 = lane < 32 && rq < T ? (uint32_t)(rq * G + g) * rowb + (lane & 7) * 16 : kPast;
+    vx1 = lane >= 32 && lane < 48 && rsr < T ? (uint32_t)(rsr * G + g) * KS + (lane & 3) * 4 : kPast;
+  }
+
+  // every load of the range at once, chunk by chunk, activations first
+  SkW<R> w[U];
+  u32x4 x0[U], x1[U];
+#pragma unroll
+  for (int c = 0; c < U; ++c) {
+    const uint32_t past = c < cnt ? 0u : kPast;
+    const int kc = c0 + min(c, cnt - 1);
+    if constexpr (AM == A_F16) {
+      x0[c] = buf_load16(rx, vx0 | past, kc * (kChunk * 2));
+      if (T > 2) x1[c] = buf_load16(rx, vx1 | past, kc * (kChunk * 2));
+    } else {
+      x0[c] = buf_load16(rx, vx0 | past, kc * (kChunk / 2));
+      x1[c][0] = buf_load4(rxs, vx1 | past, kc * 16);
+    }
+#pragma unroll
+    for (int f = 0; f < R; ++f) {
+      w[c].h0[f] = buf_load16_nt(rw, vrow | past, sw[f] + kc * 128);
+      w[c].h1[f] = buf_load16_nt(rw, vrow | past, sw[f] + kc * 128 + 8 * KB);
+      w[c].s[f] = buf_load4(rs, vs | past, ss[f] + kc * 16);
+    }
+  }
+
+  // the wave's two slots of T staged rows
+  uint8_t* slots[2] = {sk + kp * (2 * T * kSkinnyPitch), sk + kp * (2 * T * kSkinnyPitch) + T * kSkinnyPitch};
+  // stage one chunk; sh[r] = shift of row r (bf16)
+  auto stage = [&](uint8_t* slot, const u32x4& v0, const u32x4& v1, int (&sh)[kSkinnyRows]) {
+    if constexpr (AM == A_F16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && T <= 2) {
+          sh[2] = sh[3] = 0;
+          break;
+        }
+        const u32x4& v = h == 0 ? v0 : v1;
+        uint32_t mx = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = max(mx, max(v[e] & 0x7FFFu, (v[e] >> 16) & 0x7FFFu));
+        mx = row16_max(mx);
+        const uint32_t m0 = max((uint32_t)__builtin_amdgcn_readlane((int)mx, 0), (uint32_t)__builtin_amdgcn_readlane((int)mx, 16));
+        const uint32_t m1 = max((uint32_t)__builtin_amdgcn_readlane((int)mx, 32), (uint32_t)__builtin_amdgcn_readlane((int)mx, 48));
+        sh[2 * h] = shift_from_maxbits(m0 << 16);
+        sh[2 * h + 1] = shift_from_maxbits(m1 << 16);
+        const int row = 2 * h + (lane >> 5);
+        const int s = lane < 32 ? sh[2 * h] : sh[2 * h + 1];
+        f16x8 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[2 * e] = (f16)__builtin_ldexpf(bf16_bits_to_float(v[e] & 0xFFFFu), s);
+          o[2 * e + 1] = (f16)__builtin_ldexpf(bf16_bits_to_float(v[e] >> 16), s);
+        }
+        if (row < T) *reinterpret_cast<f16x8*>(slot + row * kSkinnyPitch + step_major_pos((lane & 31) * 8) * 2) = o;
+      }
+    } else {
+      // lane l < 32 decodes 32 codes of row l / 8 (blocks 2p, 2p+1, p = l % 8);
+      // their scale bytes sit in lane 32 + 4 * row + p / 2, half p % 2
+      const int rq = lane >> 3, p = lane & 7;
+      const uint32_t sw4 = (uint32_t)__shfl((int)v1[0], 32 + 4 * (rq & 3) + (p >> 1));
+      const uint32_t sb = (p & 1) ? sw4 >> 16 : sw4 & 0xFFFFu;
+      const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+      if (lane < 32 && rq < T) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f16x8*>(slot + rq * kSkinnyPitch + step_major_pos(p * 32 + 8 * j) * 2) =
+              decode8(v0[j], s2[j >> 1]);
+      }
+#pragma unroll
+      for (int r = 0; r < kSkinnyRows; ++r) sh[r] = 0;
+    }
+  };
+
+  f32x4 acc[R];
+#pragma unroll
+  for (int f = 0; f < R; ++f) acc[f] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int rd = (lr < T ? lr : 0) * kSkinnyPitch + lg * 16;   // token columns past T read row 0 (discarded)
+  auto compute = [&](SkW<R>& wc, const uint8_t* slot, const int (&sh)[kSkinnyRows]) {
+#pragma unroll
+    for (int f = 0; f < R; ++f) unshuffle_rows(wc.h0[f], wc.h1[f], (lane >> 3) & 1);
+    f16 sc[R][4];
+#pragma unroll
+    for (int f = 0; f < R; ++f) scales4(wc.s[f], sc[f]);
+    f32x4 c[R];
+#pragma unroll
+    for (int f = 0; f < R; ++f) c[f] = AM == A_F16 ? (f32x4){0.f, 0.f, 0.f, 0.f} : acc[f];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f16x8 bf = *reinterpret_cast<const f16x8*>(slot + rd + q * 64);
+#pragma unroll
+      for (int f = 0; f < R; ++f) {
+        const f16x8 af = decode8(word_of(wc.h0[f], wc.h1[f], q), sc[f][q >> 1]);
+        c[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, c[f], 0, 0, 0);
+      }
+    }
+    if constexpr (AM == A_F16) {
+      const int s = lr == 0 ? sh[0] : lr == 1 ? sh[1] : lr == 2 ? sh[2] : sh[3];
+#pragma unroll
+      for (int f = 0; f < R; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[f][i] += __builtin_ldexpf(c[f][i], -s);
+    } else {
+#pragma unroll
+      for (int f = 0; f < R; ++f) acc[f] = c[f];
+    }
+  };
+
+  // chunk c in slot c % 2; chunk c + 1 is staged before chunk c is computed
+  int sh[2][kSkinnyRows];
+  stage(slots[0], x0[0], x1[0], sh[0]);
+#pragma unroll
+  for (int c = 0; c < U; ++c) {
+    if (c >= cnt) break;
+    if (c + 1 < U && c + 1 < cnt) stage(slots[(c + 1) & 1], x0[c + 1], x1[c + 1], sh[(c + 1) & 1]);
+    compute(w[c], slots[c & 1], sh[c & 1]);
+  }
+
+  float alpha = a.w_ws2[g];
+  if (a.gsa) alpha *= a.gsa[0];
+  auto store = [&](int f, const f32x4& v) {
+    uint2 o;
+    o.x = float_to_bf16_bits(v[0] * alpha) | (float_to_bf16_bits(v[1] * alpha) << 16);
+    o.y = float_to_bf16_bits(v[2] * alpha) | (float_to_bf16_bits(v[3] * alpha) << 16);
+    *reinterpret_cast<uint2*>(a.y + (int64_t)(lr * G + g) * a.N + fbase[f] + 4 * lg) = o;
+  };
+  if (KP == 1) {
+    if (lr < T) {
+#pragma unroll
+      for (int f = 0; f < R; ++f)
+        if (fvalid[f]) store(f, acc[f]);
+    }
+    return;
+  }
+  // the range totals of each fragment, added in range order
+  __syncthreads();   // every wave is done with its slots
+  f32x4* red = reinterpret_cast<f32x4*>(sk);
+#pragma unroll
+  for (int f = 0; f < R; ++f) red[(f * KP + kp) * 64 + lane] = acc[f];
+  __syncthreads();
+  if (kp != 0 || lr >= T) return;
+#pragma unroll
+  for (int f = 0; f < R; ++f) {
+    if (!fvalid[f]) continue;
+    f32x4 v = red[f * KP * 64 + lane];
+    for (int j = 1; j < KP; ++j) {
+      const f32x4 q = red[(f * KP + j) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += q[i];
+    }
+    store(f, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
 
@@ -1099,6 +1342,65 @@ hipError_t launch_split_reduce(const float* part, int S, int64_t n, uint16_t* y,
   hipLaunchKernelGGL(nvfp4_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(part), S, n4, reinterpret_cast<uint2*>(y));
   return hipGetLastError();
+}
+
+SkinnyPlan skinny_plan(int64_t T, int64_t G, int64_t N, int64_t K, bool fp4) {
+  SkinnyPlan p;
+  (void)fp4;   // both activation forms stage the same fp16 slots
+  if (T < 1 || T > kSkinnyRows || G < 1 || N < 16 || N % 16 != 0 || K < kChunk || K % kChunk != 0) return p;
+  const int64_t nkc = K / kChunk, nfrag = N / 16;
+  // The shortest ranges the 16 waves of a workgroup and its LDS allow (one
+  // chunk per wave up to 16 chunks; measured on MI355X, more waves with less
+  // each beat fewer waves with all of K requested at once); one fragment per
+  // wave unless that gives more than about 16 waves per compute unit.
+  constexpr int64_t kWaveCap = 4096;
+  for (int64_t u = 1; u <= 4 && !p.kp_ok(); ++u) {
+    const int64_t kp = (nkc + u - 1) / u;
+    if (kp <= kSkinnyMaxWaves && kp * 2 * T * kSkinnyPitch <= kSkinnyLds && kp * 2 * 64 * 16 <= kSkinnyLds) {
+      p.u = (int)((nkc + kp - 1) / kp);
+      p.kp = (int)kp;
+    }
+  }
+  if (!p.kp_ok()) return p;
+  p.r = G * nfrag * p.kp > kWaveCap && nfrag >= 2 ? 2 : 1;
+  p.nb = (int)((nfrag + p.r - 1) / p.r);
+  p.lds = (int)std::max<int64_t>((int64_t)p.kp * 2 * T * kSkinnyPitch, p.kp > 1 ? (int64_t)p.kp * p.r * 64 * 16 : 0);
+  p.ok = G * p.nb < ((int64_t)1 << 31);
+  return p;
+}
+
+namespace {
+template <int R, int AM>
+hipError_t launch_skinny_u(const GemmArgs& a, int u, dim3 grid, dim3 block, int lds, hipStream_t s) {
+  switch (u) {
+    case 1: hipLaunchKernelGGL((nvfp4_gemm_skinny<R, 1, AM>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((nvfp4_gemm_skinny<R, 2, AM>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((nvfp4_gemm_skinny<R, 3, AM>), grid, block, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((nvfp4_gemm_skinny<R, 4, AM>), grid, block, lds, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_skinny(const GemmArgs& a, int amode, const SkinnyPlan& p, hipStream_t s) {
+  const int64_t nkc = a.K / kChunk;
+  if (!p.ok || a.gl_T < 1 || a.gl_T > kSkinnyRows || a.gl_G < 1 || a.sk_kp != p.kp || a.sk_u != p.u ||
+      a.nb != p.nb || p.u < 1 || p.u > 4 || p.kp < 1 || p.kp > kSkinnyMaxWaves ||
+      (int64_t)(p.kp - 1) * p.u >= nkc || (int64_t)p.kp * p.u < nkc || p.lds > kSkinnyLds ||
+      (int64_t)p.kp * 2 * a.gl_T * kSkinnyPitch > p.lds || (p.kp > 1 && p.kp * p.r * 64 * 16 > p.lds) ||
+      (int64_t)p.nb * p.r * 16 < a.N || (p.r != 1 && p.r != 2))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.gl_G * p.nb)), block((unsigned)(p.kp * 64));
+  if (amode == A_F16) {
+    return p.r == 1 ? launch_skinny_u<1, A_F16>(a, p.u, grid, block, p.lds, s)
+                    : launch_skinny_u<2, A_F16>(a, p.u, grid, block, p.lds, s);
+  }
+  if (amode == A_FP4) {
+    return p.r == 1 ? launch_skinny_u<1, A_FP4>(a, p.u, grid, block, p.lds, s)
+                    : launch_skinny_u<2, A_FP4>(a, p.u, grid, block, p.lds, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 int gemm_rows_per_block(int epi, GemmShape sh) {

@@ -85,6 +85,9 @@ struct GemmArgs {
   int mrows, mcols, mpass;
   unsigned* mcnt;
   int nb;              // weight-row blocks per group (grid = groups * nb)
+  // Skinny kernel (grouped linear with gl_T <= 4): workgroup = (group, R
+  // fragments); its sk_kp waves take ranges of sk_u chunks of K.
+  int sk_kp, sk_u;
   // Activation operand.
   const void* a;       // see AMode; row pitch in elements = K
   int a_rows;          // rows of the activation tensor (bounds of its buffer resource)
@@ -163,6 +166,19 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 // y[i] = bf16(sum over s = 0..S-1, in that order, of part[s * n + i]), n % 4 == 0.
 hipError_t launch_split_reduce(const float* part, int S, int64_t n, uint16_t* y, hipStream_t stream);
+
+// Launch plan of the skinny kernel (one launch per call, no workspace) for a
+// grouped linear of G groups of T <= 4 rows, or ok = false.
+struct SkinnyPlan {
+  bool ok = false;
+  int r = 1;           // fragments per wave (1 or 2)
+  int u = 0, kp = 0;   // chunks per range, ranges of K (= waves per workgroup)
+  int nb = 1;          // workgroups per group
+  int lds = 0;         // dynamic LDS bytes
+  bool kp_ok() const { return kp > 0; }
+};
+SkinnyPlan skinny_plan(int64_t T, int64_t G, int64_t N, int64_t K, bool fp4);
+hipError_t launch_gemm_skinny(const GemmArgs& a, int amode, const SkinnyPlan& p, hipStream_t stream);
 
 // Fused RMSNorm + NVFP4 quantization of x [T, K] with weight w [K]: r per row
 // into rrow [T], y [T, K] bf16 if y != nullptr, codes q [T, K/2], scale bytes

@@ -64,6 +64,23 @@ def test_linear_validation(lib):
     assert call(args(wb=4)) == -4
 
 
+def test_linear_small_row_counts_need_no_workspace(lib):
+    """Up to 4 rows per group the linear is one launch that converts its
+    activations in LDS and adds its K ranges there: no workspace.  More rows
+    take the staged kernels."""
+    L = lib
+    for m in (1, 2, 3, 4):
+        assert L.nvfp4_linear_workspace_size(m, 1536, 7168) == 0
+        assert L.nvfp4_linear_workspace_size(m, 24576, 1536) == 0
+        assert L.nvfp4_linear_workspace_size(m, 64, 8448) == 0
+        assert L.nvfp4_linear_workspace_size(m, 16, 256) == 0
+    assert L.nvfp4_grouped_linear_workspace_size(4, 8, 1024, 4096) == 0
+    assert L.nvfp4_linear_workspace_size(1, 64, 16384) == 0
+    assert L.nvfp4_linear_workspace_size(4, 64, 16384) > 0     # 16 waves x 2 slots x 4 rows exceed the LDS
+    assert L.nvfp4_linear_workspace_size(5, 1536, 7168) > 0
+    assert L.nvfp4_grouped_linear_workspace_size(5, 8, 1024, 4096) > 0
+
+
 def test_grouped_linear_validation(lib):
     L = lib
     ws = L.nvfp4_grouped_linear_workspace_size(64, 8, 1024, 4096)

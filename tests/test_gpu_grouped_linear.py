@@ -17,7 +17,8 @@ def _inputs(t, g, n, k, seed=0):
 
 
 @pytest.mark.parametrize("t,g,n,k", [
-    (1, 8, 64, 512), (4, 8, 128, 512),          # barrier-free kernel (up to 4 rows per group)
+    (1, 8, 64, 512), (4, 8, 128, 512),          # one-launch kernel (up to 4 rows per group)
+    (2, 8, 1024, 4096),                         # the same at the decode shape's K and width
     (5, 8, 128, 1024), (37, 8, 96, 1024),       # four-wave kernel; partial weight-row block
     (20, 3, 64, 768),                           # K not a multiple of 1024
     (64, 8, 1024, 4096),                        # decode shape: 8 groups, K 4096, width 1024

@@ -73,9 +73,10 @@ def test_linear_extreme_activation_range():
 @pytest.mark.parametrize("m,k", [(4, 1536), (1, 7168)])
 def test_linear_wide_binade_spread_within_a_row(m, k):
     """Rows whose magnitudes span more than 29 binades: the fp16 staging
-    shifts each row so its maximum lands in [2^14, 2^15), so elements more
-    than 29 binades below the maximum fall on fp16 subnormals (or flush to
-    zero below 2^-24 after the shift).  Each output element stays within its
+    shifts each row (each 256-element chunk of it, at most 4 rows) so its
+    maximum lands in [2^14, 2^15), so elements more than 29 binades below
+    that maximum fall on fp16 subnormals (or flush to zero below 2^-24 after
+    the shift).  Each output element stays within its
     bound, which carries 2^-39 * max|x_row| * sum_k |W[n, k]| for that
     rounding besides the accumulation and output roundings."""
     say(f"linear binade spread M={m} K={k}")
@@ -95,6 +96,88 @@ def test_linear_wide_binade_spread_within_a_row(m, k):
     ref, bound = linear_reference_and_bound(xr, li.w, li.w_sf, li.ws2)
     compare(y, ref, what=f"binade spread {m}x{k}")
     check_elementwise(y.float().cpu().numpy(), ref, bound, what=f"binade spread {m}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 1536, 7168), (4, 1536, 7168),      # projection shape: K split over the waves of a workgroup
+    (2, 24576, 1536),                      # wide projection: 6 chunks streamed by one wave
+    (3, 1552, 7424),                       # 29 chunks (last range shorter); 97 fragments (last tile half)
+    (4, 64, 8448),                         # 33 chunks
+    (4, 48, 256), (1, 16, 256),            # one chunk; one fragment
+])
+def test_linear_small_m_one_launch(m, n, k):
+    """At most 4 rows: one launch with no workspace (activations converted in
+    LDS per chunk; K up to 8 chunks streamed by one wave, longer K split over
+    the waves of a workgroup and added in LDS), bf16 and NVFP4 activations,
+    every element within its bound."""
+    say(f"linear one launch M={m} N={n} K={k}")
+    assert ops.lib().nvfp4_linear_workspace_size(m, n, k) == 0
+    li = synth.make_linear(m, n, k, seed=6)
+    w, sf, g2 = dev(li.w), dev(li.w_sf), f32(li.ws2)
+    y = ops.linear(w, sf, g2, x=dev(li.x))
+    xq, xs, gs = ops.quantize_act(dev(li.x))
+    y4 = ops.linear(w, sf, g2, x_fp4=xq, x_sf=xs, gsa=gs)
+    torch.cuda.synchronize()
+    ref, bound = linear_reference_and_bound(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
+    compare(y, ref, what=f"one launch {m}x{n}x{k}")
+    check_elementwise(y.float().cpu().numpy(), ref, bound, what=f"one launch {m}x{n}x{k}")
+    rq, rs, rgs = quant.quantize_nvfp4(li.x.float().numpy())
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
+    ref4 = linear.linear_nvfp4(rq, rs, rgs, li.w, li.w_sf, li.ws2)
+    _, bound4 = linear_reference_and_bound(quant.dequantize_nvfp4(rq, rs, rgs), li.w, li.w_sf, li.ws2, x_fp4=True)
+    compare(y4, ref4, what=f"one launch NVFP4 {m}x{n}x{k}")
+    check_elementwise(y4.float().cpu().numpy(), ref4, bound4, what=f"one launch NVFP4 {m}x{n}x{k}")
+
+
+def test_linear_four_rows_long_k_takes_the_staged_path():
+    """4 rows of K = 16384: 16 waves of 4-chunk ranges would need more LDS
+    than a workgroup has, so the call takes the staged path (fp16 copy in the
+    workspace, barrier-free kernel with a K split)."""
+    m, n, k = 4, 64, 16384
+    assert ops.lib().nvfp4_linear_workspace_size(m, n, k) > 0
+    say(f"linear staged path M={m} N={n} K={k}")
+    li = synth.make_linear(m, n, k, seed=7)
+    y = _run_bf16(li)
+    torch.cuda.synchronize()
+    ref, bound = linear_reference_and_bound(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
+    check_elementwise(y.float().cpu().numpy(), ref, bound, what="staged 4x64x16384")
+
+
+def test_linear_workspace_reused_across_shapes_and_graph_replays():
+    """One workspace serves a sequence of calls of different shapes (the
+    one-launch calls need none), and a captured graph of one-launch calls
+    replays correctly several times, with eager work in between."""
+    say("linear workspace reuse and graph replays")
+    n, k = 1536, 7168
+    need = max(ops.lib().nvfp4_linear_workspace_size(mm, n, k) for mm in (1, 4, 32))
+    work = torch.empty(need, dtype=torch.uint8, device="cuda")
+    li = synth.make_linear(32, n, k, seed=8)
+    w, sf, g2 = dev(li.w), dev(li.w_sf), f32(li.ws2)
+    x = dev(li.x)
+    ref, bound = linear_reference_and_bound(synth.bf16_to_float64(li.x), li.w, li.w_sf, li.ws2)
+    for mm in (32, 1, 4, 32, 2):
+        y = ops.linear(w, sf, g2, x=x[:mm], workspace=work)
+        torch.cuda.synchronize()
+        check_elementwise(y.float().cpu().numpy(), ref[:mm], bound[:mm], what=f"reuse M={mm}")
+    y_eager = ops.linear(w, sf, g2, x=x[:1])
+    out = torch.empty_like(y_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.linear(w, sf, g2, x=x[:1], out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(3):
+            ops.linear(w, sf, g2, x=x[:1], out=out)
+    for rep in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, y_eager), f"replay {rep}"
+        ops.linear(w, sf, g2, x=x[:4], workspace=work)   # eager work between the replays
+        torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("m,n,k", [(8, 128, 256), (128, 1536, 7168), (33, 256, 1536)])
@@ -122,9 +205,9 @@ def test_linear_empty_and_errors():
 
 @pytest.mark.parametrize("m,n,k", [(1, 1536, 7168), (32, 1536, 7168)])
 def test_linear_split_k_is_deterministic(m, n, k):
-    """Few work items split K (compact kernel at M = 1, four-wave kernel at
-    M = 32); the partial sums are added in a fixed order, so repeated calls
-    agree bit for bit."""
+    """K is split over waves (one-launch kernel at M = 1) or work items
+    (four-wave kernel at M = 32); the partial sums are added in a fixed
+    order, so repeated calls agree bit for bit."""
     say(f"linear K split determinism M={m}")
     li = synth.make_linear(m, n, k, seed=4)
     y1 = _run_bf16(li)
