@@ -348,7 +348,7 @@ int nvfp4_grouped_linear(const void* x_bf16, const uint8_t* x_fp4, const uint8_t
 
 size_t nvfp4_rmsnorm_quantize_workspace_size(int64_t T) {
   if (T <= 0 || T >= kMaxDim) return 0;
-  return round_up(sizeof(float) * (size_t)T, 256);
+  return rmsnorm_workspace_bytes((int)T);
 }
 
 int nvfp4_rmsnorm_quantize(const void* x_bf16, const void* w_bf16, float eps, int64_t T, int64_t K, void* y_bf16,
@@ -372,8 +372,7 @@ int nvfp4_rmsnorm_quantize(const void* x_bf16, const void* w_bf16, float eps, in
   if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
   return launch_status(launch_rmsnorm_quantize(static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w_bf16),
                                                eps, (int)T, (int)K, static_cast<uint16_t*>(y_bf16), gs, compute_gs,
-                                               x_fp4, x_sf, static_cast<float*>(workspace),
-                                               static_cast<hipStream_t>(stream)));
+                                               x_fp4, x_sf, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int has_shared,

@@ -101,7 +101,7 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
 // RNE_E4M3(amax_blk / (6 * gs)); codes = RNE_E2M1(x * (1 / (E4M3(byte) * gs)))
 // packed two per byte, element 2j in the low nibble.  gs == 0 or a zero scale
 // gives zero codes.  Returns the scale byte.
-__device__ __forceinline__ uint32_t quant_block16(const float (&xv)[16], float gs, uint2& packed) {
+__device__ __forceinline__ uint32_t quant_block16_sw(const float (&xv)[16], float gs, uint2& packed) {
   float ab = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) ab = fmaxf(ab, __builtin_fabsf(xv[e]));
@@ -119,6 +119,46 @@ __device__ __forceinline__ uint32_t quant_block16(const float (&xv)[16], float g
       }
     }
   }
+  return sbyte;
+}
+
+// E4M3 byte of a non-negative float, RNE, saturating at 448: the hardware
+// converter on the value clamped to 448.  Equal to e4m3_encode_nonneg for
+// every non-negative fp32 input (all 2^31 non-negative bit patterns compared
+// on MI355X; a NaN clamps to 448 in both).
+__device__ __forceinline__ uint32_t e4m3_encode_hw(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(v, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
+// The same block quantization with the hardware converters: the E2M1
+// converter (scale operand 1.0) rounds to nearest even and saturates at 6
+// exactly as e2m1_encode for every fp32 input that is not a NaN (all 2^32
+// bit patterns compared on MI355X).  Blocks holding an infinity or a NaN, and
+// scales whose reciprocal is not finite, take the software encoders, so that
+// no NaN ever reaches the converter: the result is bit-identical to
+// quant_block16_sw for every input.
+__device__ __forceinline__ uint32_t quant_block16(const float (&xv)[16], float gs, uint2& packed) {
+  uint32_t im = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) im = max(im, __float_as_uint(xv[e]) & 0x7FFFFFFFu);
+  if (im >= 0x7F800000u) return quant_block16_sw(xv, gs, packed);
+  packed = make_uint2(0u, 0u);
+  if (gs == 0.0f) return 0u;
+  const uint32_t sbyte = e4m3_encode_hw(__uint_as_float(im) / (6.0f * gs));
+  const float scale = e4m3_to_float(sbyte) * gs;
+  if (scale == 0.0f) return sbyte;
+  const float r = 1.0f / scale;
+  if (!(r <= 3.402823466e38f)) return quant_block16_sw(xv, gs, packed);
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xv[0] * r, xv[1] * r, 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xv[2] * r, xv[3] * r, 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xv[4] * r, xv[5] * r, 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xv[6] * r, xv[7] * r, 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xv[8] * r, xv[9] * r, 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xv[10] * r, xv[11] * r, 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xv[12] * r, xv[13] * r, 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xv[14] * r, xv[15] * r, 1.0f, 3);
+  packed = make_uint2(lo, hi);
   return sbyte;
 }
 
@@ -151,5 +191,7 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
+
+
 
 }  // namespace nvfp4

@@ -180,11 +180,13 @@ struct SkinnyPlan {
 SkinnyPlan skinny_plan(int64_t T, int64_t G, int64_t N, int64_t K, bool fp4);
 hipError_t launch_gemm_skinny(const GemmArgs& a, int amode, const SkinnyPlan& p, hipStream_t stream);
 
-// Fused RMSNorm + NVFP4 quantization of x [T, K] with weight w [K]: r per row
-// into rrow [T], y [T, K] bf16 if y != nullptr, codes q [T, K/2], scale bytes
-// sf [T, K/16]; gs computed (compute_gs) or read from *gs.
+// Fused RMSNorm + NVFP4 quantization of x [T, K] with weight w [K]: y [T, K]
+// bf16 if y != nullptr, codes q [T, K/2], scale bytes sf [T, K/16]; gs
+// computed (compute_gs) or read from *gs.  The workspace (rmsnorm_workspace_bytes(T))
+// holds r per row and the per-workgroup maxima of |y|.
+size_t rmsnorm_workspace_bytes(int T);
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* w, float eps, int T, int K, uint16_t* y,
-                                   float* gs, int compute_gs, uint8_t* q, uint8_t* sf, float* rrow,
+                                   float* gs, int compute_gs, uint8_t* q, uint8_t* sf, void* workspace,
                                    hipStream_t stream);
 
 // word = max |x| over n bf16 values (n % 8 == 0), as a float (zeroed first).

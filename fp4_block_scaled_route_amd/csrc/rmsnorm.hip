@@ -5,140 +5,249 @@
 // fused kernel must give the global scale and FP4 data of RMSNorm followed by
 // the activation quantizer.  So this is that composition, each rounding as in
 // the unfused path (RMSNorm's output is bf16 before it is quantized):
-//   ss  = sum_k x[k]^2 in fp64 (every square of a bf16 value is exact);
+//   ss  = sum_k x[k]^2 in fp64 (every square of a bf16 value is exact; the
+//         additions are exact while a row's squares span fewer than about
+//         37 bits, and round in this kernel's order otherwise);
 //   r   = fp32(1 / sqrt(ss / K + eps)), the root and quotient in fp64;
 //   y_k = bf16_RNE(fp32(fp32(x_k * r) * w_k));
 //   then the quantizer of quantize.hip on y (gs = amax|y| / 2688, or given).
-// Two passes over x instead of four over x and y: pass 1 (one wave per row)
-// computes r, the row's max |y| (merged with one atomic per workgroup) and
-// optionally writes y; pass 2 (one thread per 16-element block) recomputes
-// its 16 values of y from x, w and r, bit for bit, and quantizes them.
+// Two launches, two passes over x:
+//  pass 1 (a wave per row, the row held in registers, w staged in LDS once per
+//    workgroup): r of the row, the row's max |y|, y if asked for; each
+//    workgroup writes the max over its rows to its own slot (no atomics, so
+//    nothing needs clearing first);
+//  pass 2 (a thread per 16-element block, grid-strided; w again in LDS):
+//    every workgroup reduces the slots to amax (integer max of the bit
+//    patterns: exact and order-free) and gs = amax / 2688, recomputes its 16
+//    values of y from x, w and r bit for bit and quantizes them; workgroup 0
+//    writes gs.
+#include <algorithm>
+
 #include "device_util.h"
 
 namespace nvfp4 {
 
 namespace {
 
-constexpr int kRowCache = 16;   // rows of up to 16 * 512 elements stay in registers
+constexpr int kStatsWaves = 8;     // waves per pass-1 workgroup, at most
+constexpr int kMaxSlots = 512;     // pass-1 workgroups, at most (one max slot each)
+constexpr int kQuantThreads = 256;
+constexpr int kLdsW = 32768;       // bf16 weights staged in LDS (K up to this; longer K reads w from memory)
 
-__device__ __forceinline__ float norm_value(float x, float r, float w) {
-  const float xr = __fmul_rn(x, r);
-  return bf16_bits_to_float(float_to_bf16_bits(__fmul_rn(xr, w)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// y of two adjacent elements, packed bf16 (element 2j in the low half):
+// bf16_RNE(fp32(fp32(x * r) * w)); one packed conversion (NaN preserving).
+__device__ __forceinline__ uint32_t norm_pair(uint32_t xp, uint32_t wp, float r) {
+  const float lo = __fmul_rn(__fmul_rn(__uint_as_float(xp << 16), r), __uint_as_float(wp << 16));
+  const float hi = __fmul_rn(__fmul_rn(__uint_as_float(xp & 0xFFFF0000u), r), __uint_as_float(wp & 0xFFFF0000u));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-__global__ __launch_bounds__(256) void nvfp4_rmsnorm_stats(const uint16_t* x, const uint16_t* w, int T, int K,
-                                                           float eps, float* rrow, uint16_t* y, float* amax_word) {
+// w [K] into LDS (K <= kLdsW), by all threads of the workgroup, eight
+// 16-byte loads in flight per thread
+__device__ __forceinline__ void stage_w(const uint16_t* w, int K, uint16_t* wl) {
+  const int nv = K / 8;
+  for (int base = threadIdx.x; base < nv; base += blockDim.x * 8) {
+    u32x4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = min(base + j * (int)blockDim.x, nv - 1);   // (repeats the last vector past the end)
+      t[j] = *reinterpret_cast<const u32x4*>(w + i * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * (int)blockDim.x;
+      if (i < nv) *reinterpret_cast<u32x4*>(wl + i * 8) = t[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Pass 1: piece i of a lane covers columns 8 * lane + 512 * i (rows of up to
+// RC * 512 elements stay in registers; longer rows are read twice).
+template <int RC>
+__global__ __launch_bounds__(kStatsWaves * 64, 4) void nvfp4_rmsnorm_stats(const uint16_t* x, const uint16_t* w,
+                                                                          int T, int K, float eps, float* rrow,
+                                                                          uint16_t* y, unsigned* slots) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t wl[];   // K bf16 when K <= kLdsW
+  __shared__ uint32_t wmax[kStatsWaves];
+  const bool wlds = K <= kLdsW;
+  const uint16_t* wsrc = wlds ? wl : w;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  uint32_t mx = 0;   // max |y| bits of this wave's row (bf16 magnitude << 16)
-  if (t < T) {
-    const uint16_t* row = x + (int64_t)t * K;
-    const bool cached = K <= kRowCache * 512;
-    uint4 v[kRowCache];
-    double ss = 0.0;
-    auto add_sq = [&](const uint4 p) {
-      const uint32_t u[4] = {p.x, p.y, p.z, p.w};
+  const int nwv = blockDim.x >> 6;
+  const bool cached = K <= RC * 512;
+  u16x2_t mx2 = {0, 0};   // max |y| bits (bf16 magnitudes) of this wave's rows, per half
+  bool staged = !wlds;
+  for (int t = blockIdx.x * nwv + wave; t < T || !staged; t += gridDim.x * nwv) {
+    // the row's loads go out before the workgroup stages w (first row)
+    const bool has_row = t < T;
+    const uint16_t* row = x + (int64_t)(has_row ? t : 0) * K;
+    u32x4 v[RC];
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        const int c = lane * 8 + 512 * i;
+        v[i] = has_row && c < K ? *reinterpret_cast<const u32x4*>(row + c) : (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+    if (!staged) {
+      stage_w(w, K, wl);   // (every wave of the workgroup takes this branch on its first row)
+      staged = true;
+    }
+    if (!has_row) break;
+    // sum of squares: four fp64 partial sums per lane (pair e of each 16-byte
+    // piece into sum e, pieces in column order), added pairwise, then across
+    // lanes in a butterfly
+    double ss4[4] = {0.0, 0.0, 0.0, 0.0};
+    auto add_sq = [&](const u32x4 p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double a = bf16_bits_to_float(u[e] & 0xFFFFu), b = bf16_bits_to_float(u[e] >> 16);
-        ss += a * a;
-        ss += b * b;
+        const double a = __uint_as_float(p[e] << 16), b = __uint_as_float(p[e] & 0xFFFF0000u);
+        ss4[e] += a * a;
+        ss4[e] += b * b;
       }
     };
     if (cached) {
 #pragma unroll
-      for (int i = 0; i < kRowCache; ++i) {
-        const int c = lane * 8 + 512 * i;
-        v[i] = c < K ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < kRowCache; ++i) add_sq(v[i]);
+      for (int i = 0; i < RC; ++i) add_sq(v[i]);
     } else {
-      for (int c = lane * 8; c < K; c += 512) add_sq(*reinterpret_cast<const uint4*>(row + c));
+      for (int c = lane * 8; c < K; c += 512) add_sq(*reinterpret_cast<const u32x4*>(row + c));
     }
+    double ss = (ss4[0] + ss4[1]) + (ss4[2] + ss4[3]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
     const float r = (float)(1.0 / __builtin_sqrt(ss / (double)K + (double)eps));
     if (lane == 0) rrow[t] = r;
-    auto norm_piece = [&](const uint4 p, int c) {
-      const uint4 wp = *reinterpret_cast<const uint4*>(w + c);
-      const uint32_t u[4] = {p.x, p.y, p.z, p.w};
-      const uint32_t wu[4] = {wp.x, wp.y, wp.z, wp.w};
-      uint32_t o[4];
+    auto norm_piece = [&](const u32x4 p, int c) {
+      const u32x4 wp = *reinterpret_cast<const u32x4*>(wsrc + c);
+      u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = norm_value(bf16_bits_to_float(u[e] & 0xFFFFu), r, bf16_bits_to_float(wu[e] & 0xFFFFu));
-        const float hi = norm_value(bf16_bits_to_float(u[e] >> 16), r, bf16_bits_to_float(wu[e] >> 16));
-        const uint32_t lb = float_to_bf16_bits(lo), hb = float_to_bf16_bits(hi);
-        mx = max(mx, max(lb & 0x7FFFu, hb & 0x7FFFu));
-        o[e] = lb | (hb << 16);
+        o[e] = norm_pair(p[e], wp[e], r);
+        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2_t, o[e] & 0x7FFF7FFFu));
       }
-      if (y) *reinterpret_cast<uint4*>(y + (int64_t)t * K + c) = make_uint4(o[0], o[1], o[2], o[3]);
+      if (y) *reinterpret_cast<u32x4*>(y + (int64_t)t * K + c) = o;
     };
     if (cached) {
 #pragma unroll
-      for (int i = 0; i < kRowCache; ++i) {
+      for (int i = 0; i < RC; ++i) {
         const int c = lane * 8 + 512 * i;
         if (c < K) norm_piece(v[i], c);
+        __builtin_amdgcn_sched_barrier(0);   // one piece at a time: the row stays the only large live set
       }
     } else {
-      for (int c = lane * 8; c < K; c += 512) norm_piece(*reinterpret_cast<const uint4*>(row + c), c);
+      for (int c = lane * 8; c < K; c += 512) norm_piece(*reinterpret_cast<const u32x4*>(row + c), c);
     }
   }
-  if (!amax_word) return;
+  if (!slots) return;
+  uint32_t mx = max((uint32_t)mx2[0], (uint32_t)mx2[1]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  __shared__ uint32_t wmax[4];
   if (lane == 0) wmax[wave] = mx;
   __syncthreads();
-  if (threadIdx.x == 0)
-    atomicMax(reinterpret_cast<unsigned*>(amax_word), max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16);
-}
-
-// one thread per 16-element block of y
-__global__ __launch_bounds__(256) void nvfp4_rmsnorm_quant(const uint16_t* x, const uint16_t* w, const float* rrow,
-                                                           int K, int64_t nblk, const float* gs_word,
-                                                           int word_is_amax, uint8_t* q, uint8_t* sf) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblk) return;
-  const int kb = K / 16;
-  const int64_t t = b / kb;
-  const int c = (int)(b - t * kb) * 16;
-  const float gs = word_is_amax ? gs_word[0] / 2688.0f : gs_word[0];
-  const float r = rrow[t];
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * K + c);
-  const uint4* wsrc = reinterpret_cast<const uint4*>(w + c);
-  const uint4 v0 = src[0], v1 = src[1], w0 = wsrc[0], w1 = wsrc[1];
-  const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  const uint32_t wu[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  float yv[16];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    yv[2 * e] = norm_value(bf16_bits_to_float(u[e] & 0xFFFFu), r, bf16_bits_to_float(wu[e] & 0xFFFFu));
-    yv[2 * e + 1] = norm_value(bf16_bits_to_float(u[e] >> 16), r, bf16_bits_to_float(wu[e] >> 16));
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < nwv; ++i) m = max(m, wmax[i]);
+    slots[blockIdx.x] = m << 16;   // fp32 bits of the workgroup's max |y|
   }
-  uint2 packed;
-  const uint32_t sbyte = quant_block16(yv, gs, packed);
-  reinterpret_cast<uint2*>(q)[b] = packed;
-  sf[b] = (uint8_t)sbyte;
 }
 
-__global__ void nvfp4_rmsnorm_gs_zero(float* gs) { gs[0] = 0.0f; }
-__global__ void nvfp4_rmsnorm_gs_finish(float* gs) { gs[0] = gs[0] / 2688.0f; }
+// Pass 2: blocks of 16 elements of y, grid-strided; gs from the slots
+// (compute_gs) or the word.
+__global__ __launch_bounds__(kQuantThreads) void nvfp4_rmsnorm_quant(const uint16_t* x, const uint16_t* w,
+                                                                     const float* rrow, int K, int64_t nblk,
+                                                                     const unsigned* slots, int nslots, float* gs_word,
+                                                                     uint8_t* q, uint8_t* sf) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t wl[];   // K bf16 when K <= kLdsW
+  __shared__ float s_gs;
+  const bool wlds = K <= kLdsW;
+  if (wlds) stage_w(w, K, wl);
+  if (threadIdx.x < 64) {
+    float g;
+    if (slots) {
+      uint32_t m = 0;
+      for (int i = threadIdx.x; i < nslots; i += 64) m = max(m, slots[i]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+      g = __uint_as_float(m) / 2688.0f;
+      if (blockIdx.x == 0 && threadIdx.x == 0) gs_word[0] = g;
+    } else {
+      g = gs_word[0];
+    }
+    if (threadIdx.x == 0) s_gs = g;
+  }
+  __syncthreads();
+  const float gs = s_gs;
+  const uint16_t* wsrc = wlds ? wl : w;
+  const int kb = K / 16;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = b / kb;
+    const int c = (int)(b - t * kb) * 16;
+    const float r = rrow[t];
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + t * K + c);
+    const u32x4* wp = reinterpret_cast<const u32x4*>(wsrc + c);
+    const u32x4 v0 = src[0], v1 = src[1], w0 = wp[0], w1 = wp[1];
+    float yv[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ya = norm_pair(v0[e], w0[e], r), yb = norm_pair(v1[e], w1[e], r);
+      yv[2 * e] = __uint_as_float(ya << 16);
+      yv[2 * e + 1] = __uint_as_float(ya & 0xFFFF0000u);
+      yv[8 + 2 * e] = __uint_as_float(yb << 16);
+      yv[8 + 2 * e + 1] = __uint_as_float(yb & 0xFFFF0000u);
+    }
+    uint2 packed;
+    const uint32_t sbyte = quant_block16(yv, gs, packed);
+    reinterpret_cast<uint2*>(q)[b] = packed;
+    sf[b] = (uint8_t)sbyte;
+  }
+}
+
+__global__ void nvfp4_rmsnorm_gs_empty(float* gs) { gs[0] = 0.0f; }
 
 }  // namespace
 
+size_t rmsnorm_workspace_bytes(int T) {
+  return (((size_t)T * sizeof(float) + 255) / 256) * 256 + kMaxSlots * sizeof(unsigned);
+}
+
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, const uint16_t* w, float eps, int T, int K, uint16_t* y,
-                                   float* gs, int compute_gs, uint8_t* q, uint8_t* sf, float* rrow, hipStream_t s) {
-  if (compute_gs) hipLaunchKernelGGL(nvfp4_rmsnorm_gs_zero, dim3(1), dim3(1), 0, s, gs);
-  if (T <= 0) return hipGetLastError();
-  hipLaunchKernelGGL(nvfp4_rmsnorm_stats, dim3((T + 3) / 4), dim3(256), 0, s, x, w, T, K, eps, rrow, y,
-                     compute_gs ? gs : nullptr);
+                                   float* gs, int compute_gs, uint8_t* q, uint8_t* sf, void* workspace,
+                                   hipStream_t s) {
+  if (T <= 0) {
+    // no elements: amax = 0
+    if (compute_gs) hipLaunchKernelGGL(nvfp4_rmsnorm_gs_empty, dim3(1), dim3(1), 0, s, gs);
+    return hipGetLastError();
+  }
+  float* rrow = static_cast<float*>(workspace);
+  unsigned* slots = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(workspace) +
+                                                (((size_t)T * sizeof(float) + 255) / 256) * 256);
+  // a wave per row, spread over up to kMaxSlots workgroups of up to 8 waves
+  const int wpg = std::min(kStatsWaves, std::max(1, (T + kMaxSlots - 1) / kMaxSlots));
+  const int g1 = std::min(kMaxSlots, (T + wpg - 1) / wpg);
+  const size_t lds = K <= kLdsW ? (size_t)K * 2 : 0;
+  const dim3 grid1(g1), block1(wpg * 64);
+  unsigned* sl = compute_gs ? slots : nullptr;
+  // the row cache sized to K (rows of up to 8192 elements stay in registers)
+  const int pieces = (K + 511) / 512;
+  if (pieces <= 2)
+    hipLaunchKernelGGL(nvfp4_rmsnorm_stats<2>, grid1, block1, lds, s, x, w, T, K, eps, rrow, y, sl);
+  else if (pieces <= 4)
+    hipLaunchKernelGGL(nvfp4_rmsnorm_stats<4>, grid1, block1, lds, s, x, w, T, K, eps, rrow, y, sl);
+  else if (pieces <= 8)
+    hipLaunchKernelGGL(nvfp4_rmsnorm_stats<8>, grid1, block1, lds, s, x, w, T, K, eps, rrow, y, sl);
+  else if (pieces <= 14)
+    hipLaunchKernelGGL(nvfp4_rmsnorm_stats<14>, grid1, block1, lds, s, x, w, T, K, eps, rrow, y, sl);
+  else
+    hipLaunchKernelGGL(nvfp4_rmsnorm_stats<16>, grid1, block1, lds, s, x, w, T, K, eps, rrow, y, sl);
   const int64_t nblk = (int64_t)T * (K / 16);
-  hipLaunchKernelGGL(nvfp4_rmsnorm_quant, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, x, w, rrow, K, nblk,
-                     gs, compute_gs, q, sf);
-  if (compute_gs) hipLaunchKernelGGL(nvfp4_rmsnorm_gs_finish, dim3(1), dim3(1), 0, s, gs);
+  const int64_t g2 = std::max<int64_t>(1, std::min<int64_t>(2048, (nblk + kQuantThreads - 1) / kQuantThreads));
+  hipLaunchKernelGGL(nvfp4_rmsnorm_quant, dim3((unsigned)g2), dim3(kQuantThreads), lds, s, x, w, rrow, K, nblk, sl,
+                     g1, gs, q, sf);
   return hipGetLastError();
 }
 

@@ -106,7 +106,8 @@ int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int 
  *   y_bf16 [T, K]: optional output of y (NULL: not written).
  *   gs, compute_gs, x_fp4 [T, K/2], x_sf [T, K/16]: as nvfp4_quantize_act,
  *   applied to y.
- *   workspace: nvfp4_rmsnorm_quantize_workspace_size(T) bytes (r per row).
+ *   workspace: nvfp4_rmsnorm_quantize_workspace_size(T) bytes (r per row and
+ *   the per-workgroup maxima of |y|; scratch, undefined after the call).
  * T == 0 writes nothing but gs, which compute_gs sets to 0 (no elements);
  * every other pointer may then be NULL.
  * Requires K % 16 == 0 (K % 256 == 0 to feed nvfp4_linear), eps > 0 and
