@@ -724,6 +724,7 @@ def run_rmsnorm_quant(args, cfg):
     y = torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
     work = torch.empty(max(16, ops.lib().nvfp4_rmsnorm_quantize_workspace_size(t)), dtype=torch.uint8, device="cuda")
     L = ops.lib()
+    qwork = torch.empty(max(16, L.nvfp4_quantize_act_workspace_size(t, k)), dtype=torch.uint8, device="cuda")
 
     def fused(i):
         s = torch.cuda.current_stream().cuda_stream
@@ -736,7 +737,8 @@ def run_rmsnorm_quant(args, cfg):
         ops._check(L.nvfp4_rmsnorm_quantize(xs[i % copies].data_ptr(), w.data_ptr(), eps, t, k, y.data_ptr(),
                                             gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), work.data_ptr(),
                                             work.numel(), s))
-        ops._check(L.nvfp4_quantize_act(y.data_ptr(), t, k, gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(), s))
+        ops._check(L.nvfp4_quantize_act(y.data_ptr(), t, k, gs.data_ptr(), 1, q.data_ptr(), sf.data_ptr(),
+                                        qwork.data_ptr(), qwork.numel(), s))
 
     ms_eager = time_eager(fused, args.warmup, args.steps)
     ms = time_graph(fused, args.steps)

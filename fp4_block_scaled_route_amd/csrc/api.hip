@@ -124,17 +124,26 @@ const char* nvfp4_status_string(int status) {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
+size_t nvfp4_quantize_act_workspace_size(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || M >= kMaxDim || K >= kMaxDim) return 0;
+  return quantize_workspace_bytes();
+}
+
 int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int compute_gs, uint8_t* x_fp4,
-                       uint8_t* x_sf, void* stream) {
-  if (M < 0 || K <= 0 || K % 16 != 0 || M >= kMaxDim || K >= kMaxDim) return NVFP4_ERR_SHAPE;
+                       uint8_t* x_sf, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || K <= 0 || K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || M * K >= kMaxDim) return NVFP4_ERR_SHAPE;
   if (!gs) return NVFP4_ERR_NULL;
   if (!aligned(gs, 4)) return NVFP4_ERR_ALIGN;
   if (M > 0) {
     if (!x_bf16 || !x_fp4 || !x_sf) return NVFP4_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(x_fp4, 8)) return NVFP4_ERR_ALIGN;
+    if (compute_gs) {
+      if (!workspace || workspace_bytes < nvfp4_quantize_act_workspace_size(M, K)) return NVFP4_ERR_WORKSPACE;
+      if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+    }
   }
   return launch_status(launch_quantize_act(static_cast<const uint16_t*>(x_bf16), M, K, gs, compute_gs, x_fp4,
-                                           x_sf, static_cast<hipStream_t>(stream)));
+                                           x_sf, static_cast<unsigned*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_router_prepare(const void* w_bf16, int64_t E, int64_t H, float* scale, void* w_rt_bf16, void* stream) {

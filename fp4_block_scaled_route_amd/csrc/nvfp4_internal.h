@@ -204,7 +204,11 @@ int router_ksplit(int T, int H, int E);
 hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_rt, int T, int H, int E, int topk, float* logits,
                               int32_t* ids, float* wts, float* part, hipStream_t stream);
 
+// NVFP4 quantization of x [M, K]; with compute_gs the per-workgroup maxima of
+// |x| go to slots (quantize_workspace_bytes()) and gs = amax / 2688 is
+// written to *gs, else *gs is read.
+size_t quantize_workspace_bytes();
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, float* gs, int compute_gs,
-                               uint8_t* q, uint8_t* sf, hipStream_t stream);
+                               uint8_t* q, uint8_t* sf, unsigned* slots, hipStream_t stream);
 
 }  // namespace nvfp4

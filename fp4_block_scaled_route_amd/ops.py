@@ -22,6 +22,7 @@ _c_ptr = ctypes.c_void_p
 EXPORTED = (
     "nvfp4_status_string",
     "nvfp4_abi_version",
+    "nvfp4_quantize_act_workspace_size",
     "nvfp4_quantize_act",
     "nvfp4_rmsnorm_quantize_workspace_size",
     "nvfp4_rmsnorm_quantize",
@@ -36,7 +37,7 @@ EXPORTED = (
     "nvfp4_router_workspace_size",
     "nvfp4_router_topk",
 )
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class Nvfp4Error(RuntimeError):
@@ -137,8 +138,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_status_string.argtypes = [ctypes.c_int]
         L.nvfp4_abi_version.restype = ctypes.c_int
         L.nvfp4_abi_version.argtypes = []
+        L.nvfp4_quantize_act_workspace_size.restype = ctypes.c_size_t
+        L.nvfp4_quantize_act_workspace_size.argtypes = [_c_i64, _c_i64]
         L.nvfp4_quantize_act.restype = ctypes.c_int
-        L.nvfp4_quantize_act.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr]
+        L.nvfp4_quantize_act.argtypes = [_c_ptr, _c_i64, _c_i64, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr,
+                                         ctypes.c_size_t, _c_ptr]
         L.nvfp4_rmsnorm_quantize_workspace_size.restype = ctypes.c_size_t
         L.nvfp4_rmsnorm_quantize_workspace_size.argtypes = [_c_i64]
         L.nvfp4_rmsnorm_quantize.restype = ctypes.c_int
@@ -194,18 +198,20 @@ def status_string(status: int) -> str:
 
 
 def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
-                 out: Optional[Sequence[torch.Tensor]] = None, gs_out: Optional[torch.Tensor] = None):
+                 out: Optional[Sequence[torch.Tensor]] = None, gs_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
     """NVFP4-quantize bf16 activations [M, K].  ``gs`` None: the global scale is
     computed on the device (max|x| / 2688) into ``gs_out`` (allocated if not
     given) and returned; otherwise ``gs`` (a 1-element fp32 device tensor) is
-    used.  Returns (codes [M,K/2] u8, scales [M,K/16] u8, gs [1] fp32)."""
+    used.  ``workspace``: nvfp4_quantize_act_workspace_size bytes (allocated if
+    not given).  Returns (codes [M,K/2] u8, scales [M,K/16] u8, gs [1] fp32)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D tensor [M, K]")
     m, k = x.shape
     q, sf = out if out is not None else (None, None)
     dev = _validate([("x", x, _BF16, (m, k), True), ("gs", gs, _F32, SCALAR, False),
                      ("out[0]", q, _U8, (m, k // 2), False), ("out[1]", sf, _U8, (m, k // 16), False),
-                     ("gs_out", gs_out, _F32, SCALAR, False)])
+                     ("gs_out", gs_out, _F32, SCALAR, False), ("workspace", workspace, _U8, ("min", 0), False)])
     if out is None:
         q = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
         sf = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
@@ -214,7 +220,14 @@ def quantize_act(x: torch.Tensor, gs: Optional[torch.Tensor] = None,
         gsb = gs_out if gs_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
     else:
         gsb = gs
-    _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _stream(dev)))
+    need = lib().nvfp4_quantize_act_workspace_size(m, k) if compute else 0
+    if workspace is not None and workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() if workspace is not None else 0
+    _check(lib().nvfp4_quantize_act(_p(x), m, k, _p(gsb), int(compute), _p(q), _p(sf), _p(workspace), wsb,
+                                    _stream(dev)))
     return q, sf, gsb
 
 

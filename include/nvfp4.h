@@ -71,7 +71,7 @@ const char* nvfp4_status_string(int status);
 
 /* Host: ABI version of this header (incremented on incompatible changes). */
 int nvfp4_abi_version(void);
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 /*
  * nvfp4_quantize_act - quantize bf16 activations to NVFP4.
@@ -87,13 +87,17 @@ int nvfp4_abi_version(void);
  *   gs         device fp32 scalar: output when compute_gs != 0 (written with
  *              max|x| / 2688 computed on the device), input otherwise.
  *   x_fp4      [M, K/2] output codes; x_sf [M, K/16] output scale bytes.
+ *   workspace  device scratch of nvfp4_quantize_act_workspace_size(M, K)
+ *              bytes, 16-byte aligned, when compute_gs != 0 (per-workgroup
+ *              maxima of |x|; undefined after the call); may be NULL otherwise.
  * M == 0 writes nothing but gs, which compute_gs sets to 0 (no elements);
- * x_bf16, x_fp4 and x_sf may then be NULL.
+ * x_bf16, x_fp4, x_sf and workspace may then be NULL.
  * Requires K % 16 == 0 (K % 256 == 0 if the result feeds nvfp4_linear or
  * nvfp4_moe_grouped).
  */
+size_t nvfp4_quantize_act_workspace_size(int64_t M, int64_t K);
 int nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, float* gs, int compute_gs,
-                       uint8_t* x_fp4, uint8_t* x_sf, void* stream);
+                       uint8_t* x_fp4, uint8_t* x_sf, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * nvfp4_rmsnorm_quantize - RMSNorm fused with nvfp4_quantize_act (page

@@ -131,10 +131,14 @@ def test_rmsnorm_quantize_validation(lib):
 
 def test_quantize_validation(lib):
     L = lib
-    assert L.nvfp4_quantize_act(FAKE, 4, 40, FAKE, 1, FAKE, FAKE, None) == -2
-    assert L.nvfp4_quantize_act(FAKE, 4, 64, None, 1, FAKE, FAKE, None) == -1
-    assert L.nvfp4_quantize_act(None, 4, 64, FAKE, 1, FAKE, FAKE, None) == -1
-    assert L.nvfp4_quantize_act(ctypes.c_void_p(0x1002), 4, 64, FAKE, 1, FAKE, FAKE, None) == -3
+    ws = L.nvfp4_quantize_act_workspace_size(4, 64)
+    assert ws > 0 and L.nvfp4_quantize_act_workspace_size(0, 64) == 0
+    assert L.nvfp4_quantize_act(FAKE, 4, 40, FAKE, 1, FAKE, FAKE, FAKE, ws, None) == -2
+    assert L.nvfp4_quantize_act(FAKE, 4, 64, None, 1, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.nvfp4_quantize_act(None, 4, 64, FAKE, 1, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.nvfp4_quantize_act(ctypes.c_void_p(0x1002), 4, 64, FAKE, 1, FAKE, FAKE, FAKE, ws, None) == -3
+    assert L.nvfp4_quantize_act(FAKE, 4, 64, FAKE, 1, FAKE, FAKE, None, 0, None) == -4     # computed gs needs it
+    assert L.nvfp4_quantize_act(FAKE, 4, 64, FAKE, 1, FAKE, FAKE, FAKE, ws - 1, None) == -4
 
 
 def test_moe_validation(lib):
