@@ -83,3 +83,37 @@ def test_feeds_the_linear():
     _, rq, rs, rg = rmsnorm.rmsnorm_quantize(x.float().numpy(), w.float().numpy(), EPS)
     ref = linear.linear_nvfp4(rq, rs, float(rg), li.w, li.w_sf, li.ws2)
     compare(ylin, ref, what="rmsnorm -> linear")
+
+
+def test_wide_spread_rows_r_within_one_ulp():
+    """Rows whose squares span far more than fp64's 53 bits: the fp64 sums of
+    squares are then inexact, and the kernel's summation order (four partial
+    sums per lane, then across lanes) and the oracle's (numpy's pairwise sum)
+    may differ in the last bit.  r stays within one fp32 ulp of the oracle's
+    (the workspace's first T floats hold r per row), and y is bit-exact in
+    every row where r is."""
+    t, k = 64, 7168
+    say(f"rmsnorm wide-spread rows T={t} K={k}")
+    rng = np.random.default_rng(11)
+    x = synth.bf16_normal((t, k), 11).float()
+    x *= torch.from_numpy(np.exp2(rng.integers(-60, 11, size=(t, k))).astype(np.float32))
+    x = x.to(torch.bfloat16)
+    _, w = _inputs(1, k, seed=12)
+    xs = x.float().numpy().astype(np.float64) ** 2
+    spread = xs.max(axis=1) / np.where(xs > 0, xs, np.inf).min(axis=1)
+    assert (spread > 2.0 ** 100).all(), "rows must span more than the exact fp64 sum range"
+    work = torch.empty(ops.lib().nvfp4_rmsnorm_quantize_workspace_size(t), dtype=torch.uint8, device="cuda")
+    y = torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
+    q, sf, gs = ops.rmsnorm_quantize(x.cuda(), w.cuda(), EPS, y=y, workspace=work)
+    torch.cuda.synchronize()
+    r_gpu = work[:4 * t].view(torch.float32).cpu().numpy()
+    r_ref = rmsnorm.rms_scale(x.float().numpy(), EPS)
+    assert np.all(np.abs(r_gpu.astype(np.float64) - r_ref) <= np.abs(np.spacing(r_ref))), "r within one ulp"
+    eq = r_gpu == r_ref
+    ry = rmsnorm.rmsnorm_bf16(x.float().numpy(), w.float().numpy(), EPS)
+    assert np.array_equal(y.float().cpu().numpy()[eq], ry[eq])
+    say(f"  rows with r equal to the oracle's: {int(eq.sum())} of {t}")
+    if eq.all():
+        _, rq, rs, rg = rmsnorm.rmsnorm_quantize(x.float().numpy(), w.float().numpy(), EPS)
+        assert gs.item() == float(rg)
+        assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(sf.cpu().numpy(), rs)
