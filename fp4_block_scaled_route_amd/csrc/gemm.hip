@@ -1018,7 +1018,43 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
         }
       }
     }
-    epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
+    if constexpr (EP == EPI_SLOT && NW == 8 && R == 4) {
+      // Down GEMM, eight waves: the workgroup's outputs (the pass's token
+      // rows x its 512 weight rows, bf16) go through LDS, so that each row's
+      // 1 KB leaves in one store instruction of 16 bytes per lane instead of
+      // 16-row x 32-byte pieces (every LDS buffer is free: the last barrier
+      // of the K loop has passed).
+      constexpr int kTilePitch = 512 * 2 + 16;
+      static_assert(PR * kTilePitch <= 2 * SROWS * RSTEP * kLdsRow, "output tile fits the staging buffers");
+      static_assert(NW * R * 16 == 512, "512 weight rows per workgroup");
+      uint8_t* tile = &lds[0][0];
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int tr = 16 * c + lr;   // token row of the pass
+        if (c >= nc || pbase + tr >= it.m) continue;
+        const int sh = shift_of(a, a_row_of(a, it.row0 + pbase + tr));
+#pragma unroll
+        for (int f = 0; f < R; ++f) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh) * it.alpha;
+          uint2 o;
+          o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+          o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<uint2*>(tile + tr * kTilePitch + ((wave * R + f) * 16 + 4 * lg) * 2) = o;
+        }
+      }
+      __syncthreads();
+      const int n0 = nbk * 512 + lane * 8;
+      for (int tr = wave; tr < prow; tr += NW) {
+        const int pid = a.perm[it.row0 + pbase + tr];
+        const u32x4 o = *reinterpret_cast<const u32x4*>(tile + tr * kTilePitch + lane * 16);
+        if (n0 < a.N) *reinterpret_cast<u32x4*>(a.slot + (int64_t)pid * a.N + n0) = o;
+      }
+      if (pass + 1 < npass) __syncthreads();   // the next pass stages into these buffers
+    } else {
+      epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
+    }
   }
 }
 

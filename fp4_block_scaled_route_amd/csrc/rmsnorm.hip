@@ -5,9 +5,12 @@
 // fused kernel must give the global scale and FP4 data of RMSNorm followed by
 // the activation quantizer.  So this is that composition, each rounding as in
 // the unfused path (RMSNorm's output is bf16 before it is quantized):
-//   ss  = sum_k x[k]^2 in fp64 (every square of a bf16 value is exact; the
-//         additions are exact while a row's squares span fewer than about
-//         37 bits, and round in this kernel's order otherwise);
+//   ss  = sum_k x[k]^2 in fp64 (every square of a bf16 value is exact, a
+//         16-bit significand; the additions are exact while the row's squares
+//         fit one 53-bit fixed point with the carries of K terms, i.e. their
+//         exponents span at most 53 - 16 - ceil(log2 K) bits: 24 for K = 7168,
+//         x within about 12 binades of the row's largest |x|; otherwise they
+//         round, in this kernel's order);
 //   r   = fp32(1 / sqrt(ss / K + eps)), the root and quotient in fp64;
 //   y_k = bf16_RNE(fp32(fp32(x_k * r) * w_k));
 //   then the quantizer of quantize.hip on y (gs = amax|y| / 2688, or given).
