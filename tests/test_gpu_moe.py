@@ -127,6 +127,7 @@ def test_moe_small_fully_fp4_and_calibration():
 @pytest.mark.parametrize("t,h,i,e,k,seed", [
     (160, 1024, 1024, 24, 4, 11),   # K multiple of 1024: eight-wave kernel for both GEMMs
     (150, 512, 256, 20, 3, 12),     # four-wave large-batch configuration
+    (160, 1280, 1024, 24, 4, 14),   # eight-wave down GEMM with a ragged last 512-row block (H = 1280)
 ])
 def test_moe_large_batch_with_tiny_groups(t, h, i, e, k, seed):
     """More than 16 rows per group on average sends every group, including
