@@ -136,6 +136,45 @@ __global__ __launch_bounds__(256) void nvfp4_router_logits(const uint16_t* x, co
   }
 }
 
+// Largest (value, -index) pair of the wave, in every lane: rotations within
+// each 16-lane row (DPP row_ror 8, 4, 2, 1), then the partner row and the
+// partner half through the lane-swap instructions (no LDS round trips; the
+// comparison is the same in every step, so the order of the steps does not
+// change the result).
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+template <int R>
+__device__ __forceinline__ void row_ror_step(float& bv, int& bi) {
+  // DPP row_ror:R (lane l of a 16-lane row reads lane (l + R) % 16 of that row)
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), 0x120 + R, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, 0x120 + R, 0xF, 0xF, false);
+  take_better(bv, bi, ov, oi);
+}
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi, int lane) {
+  row_ror_step<8>(bv, bi);
+  row_ror_step<4>(bv, bi);
+  row_ror_step<2>(bv, bi);
+  row_ror_step<1>(bv, bi);
+  {
+    // rows 0<->1, 2<->3: vdst gets rows (0, 0, 2, 2), vsrc rows (1, 1, 3, 3) of the value
+    const auto v = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, bv), __builtin_bit_cast(unsigned, bv), false, false);
+    const auto i = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    const bool odd = (lane >> 4) & 1;
+    take_better(bv, bi, __builtin_bit_cast(float, odd ? v[0] : v[1]), (int)(odd ? i[0] : i[1]));
+  }
+  {
+    // halves: vdst gets (low, low), vsrc (high, high)
+    const auto v = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, bv), __builtin_bit_cast(unsigned, bv), false, false);
+    const auto i = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
+    const bool high = lane >= 32;
+    take_better(bv, bi, __builtin_bit_cast(float, high ? v[0] : v[1]), (int)(high ? i[0] : i[1]));
+  }
+}
+
 // Top-k softmax: one workgroup of 4 waves per token.  Wave w adds the
 // K-split partials s = w, w + 4, w + 8, ... in increasing s (4 splits per
 // batch of loads); wave 0 then adds the four wave sums in wave order (a fixed
@@ -203,15 +242,7 @@ __global__ __launch_bounds__(256) void nvfp4_router_select(const float* part, in
         bi = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi, lane);
     if ((bi & 63) == lane) {
 #pragma unroll
       for (int j = 0; j < kMaxPerLane; ++j)
