@@ -10,6 +10,13 @@
 
 namespace nvfp4 {
 
+// Each slot row is read once, here, so its loads carry the non-temporal hint
+// (measured on MI355X: the 4096-token combine 0.098-0.101 -> 0.090 ms).
+__device__ __forceinline__ uint4 load_slot(const uint16_t* p) {
+  const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+
 // KMAX > 0 (topk <= KMAX): all row loads of the token are issued before the
 // first use, so a wave has topk + 1 requests in flight instead of one; the
 // sum still runs in the order j = 0..topk-1, then the shared row.  KMAX == 0:
@@ -44,11 +51,10 @@ __global__ __launch_bounds__(256) void nvfp4_moe_combine(const CombineArgs a) {
     for (int j = 0; j < KMAX; ++j) {
       const int id = j < a.topk ? a.ids[t * a.topk + j] : -1;
       ok[j] = id >= 0 && id < a.E;
-      v[j] = ok[j] ? *reinterpret_cast<const uint4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n)
-                   : make_uint4(0u, 0u, 0u, 0u);
+      v[j] = ok[j] ? load_slot(a.slot + (int64_t)(t * a.topk + j) * a.H + n) : make_uint4(0u, 0u, 0u, 0u);
     }
     uint4 vs = make_uint4(0u, 0u, 0u, 0u);
-    if (a.shared) vs = *reinterpret_cast<const uint4*>(a.slot + (int64_t)(P + t) * a.H + n);
+    if (a.shared) vs = load_slot(a.slot + (int64_t)(P + t) * a.H + n);
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (ok[j]) add(v[j], a.w[t * a.topk + j]);
@@ -57,9 +63,9 @@ __global__ __launch_bounds__(256) void nvfp4_moe_combine(const CombineArgs a) {
     for (int j = 0; j < a.topk; ++j) {
       const int id = a.ids[t * a.topk + j];
       if (id < 0 || id >= a.E) continue;
-      add(*reinterpret_cast<const uint4*>(a.slot + (int64_t)(t * a.topk + j) * a.H + n), a.w[t * a.topk + j]);
+      add(load_slot(a.slot + (int64_t)(t * a.topk + j) * a.H + n), a.w[t * a.topk + j]);
     }
-    if (a.shared) add_shared(*reinterpret_cast<const uint4*>(a.slot + (int64_t)(P + t) * a.H + n));
+    if (a.shared) add_shared(load_slot(a.slot + (int64_t)(P + t) * a.H + n));
   }
   uint4 o;
   o.x = float_to_bf16_bits(acc[0]) | (float_to_bf16_bits(acc[1]) << 16);
