@@ -20,8 +20,9 @@
 // take consecutive ranges (three launches: counts per workgroup and expert; a
 // scan over the workgroups; ranks), so the rows of a group still come in pair
 // order.  The group offsets also give the processing order of the groups for
-// the GEMM (non-empty groups, largest first, ties by id), so that the GEMM
-// grid needs no host synchronisation.  Extra workgroups compute the per-row
+// the GEMM (non-empty groups, largest first by a counting sort over the
+// sizes, ties by id), so that the GEMM grid needs no host synchronisation.
+// Extra workgroups compute the per-row
 // staging shifts of the bf16 activations and clear the row-max buffer of the
 // hidden activations.
 #include <algorithm>
@@ -261,11 +262,16 @@ __device__ void rank_pairs(const PermuteArgs& a, int b0, int b1, PermLds& L) {
 
 // Phase 4, with the group offsets in L.base: the shared expert's rows, the
 // offsets, and the processing order of the groups for the GEMM (non-empty
-// groups, largest first, ties by id), so that the GEMM grid needs no host
-// synchronisation.  Group g's rank counts the groups before it; the sizes are
-// read four at a time (one 16-byte LDS read, the same address in every lane).
+// groups, largest first, ties by id; sizes of kSizeKeys - 1 rows or more
+// count as equal), so that the GEMM grid needs no host synchronisation.  A
+// counting sort: the groups per size (LDS atomics, order-free), an exclusive
+// scan over the sizes from the largest down gives each size's first list
+// position, and one wave places the groups in id order, 64 at a time (lanes
+// of equal size find each other with one ballot per size bit and take
+// consecutive positions in lane order).
+constexpr int kSizeKeys = 4096;
 __device__ void finish_groups(const PermuteArgs& a, PermLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.T * a.topk;
   const int pv = L.base[E];
   if (a.shared) {
@@ -281,21 +287,64 @@ __device__ void finish_groups(const PermuteArgs& a, PermLds& L) {
   }
   const int G = E + (a.shared ? 1 : 0);
   const int G4 = (G + 3) & ~3;
+  // the per-wave histograms are free now: counts per size, then per-wave sums
+  static_assert(sizeof(L.hist) >= (kSizeKeys + 64) * sizeof(int), "size keys fit the histogram rows");
+  int* cnt = &L.hist[0][0];
+  int* wsum = cnt + kSizeKeys;
+  __syncthreads();   // (the ranks of phase 3 read L.hist)
+  for (int i = tid; i < kSizeKeys; i += blockDim.x) cnt[i] = 0;
   for (int h = tid; h < G4; h += blockDim.x) L.gsize[h] = h < G ? L.base[h + 1] - L.base[h] : -1;
   __syncthreads();
   for (int g = tid; g < G; g += blockDim.x) {
-    const int mg = L.gsize[g];
-    if (mg <= 0) continue;
-    int rank = 0;
-#pragma unroll 4
-    for (int h = 0; h < G4; h += 4) {
-      const int4 m4 = *reinterpret_cast<const int4*>(&L.gsize[h]);
-      rank += (m4.x > mg) || (m4.x == mg && h < g);
-      rank += (m4.y > mg) || (m4.y == mg && h + 1 < g);
-      rank += (m4.z > mg) || (m4.z == mg && h + 2 < g);
-      rank += (m4.w > mg) || (m4.w == mg && h + 3 < g);
+    const int m = L.gsize[g];
+    if (m > 0) atomicAdd(&cnt[min(m, kSizeKeys - 1)], 1);
+  }
+  __syncthreads();
+  // exclusive scan from the largest size down: thread j takes the sizes
+  // kSizeKeys - 1 - (per*j .. per*j + per - 1)
+  {
+    const int nthr = blockDim.x, per = kSizeKeys / nthr;   // (the 1024-thread workgroups: 4 sizes each)
+    int s = 0;
+    for (int u = 0; u < per; ++u) s += cnt[kSizeKeys - 1 - (per * tid + u)];
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
     }
-    a.glist[rank] = g;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    int run = before + incl - s;
+    for (int u = 0; u < per; ++u) {
+      const int key = kSizeKeys - 1 - (per * tid + u);
+      const int c = cnt[key];
+      cnt[key] = run;   // first list position of this size
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int c0 = 0; c0 < G; c0 += 64) {
+      const int g = c0 + lane;
+      const int m = g < G ? L.gsize[g] : 0;
+      const bool valid = m > 0;
+      const int key = min(max(m, 0), kSizeKeys - 1);
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 12; ++b) {
+        const uint64_t bal = __ballot(valid && ((key >> b) & 1));
+        peers &= ((key >> b) & 1) ? bal : ~bal;
+      }
+      if (valid) {
+        const int pos = cnt[key] + __popcll(peers & ((1ull << lane) - 1ull));
+        a.glist[pos] = g;
+        if ((peers >> lane) == 1ull) cnt[key] += __popcll(peers);   // the highest lane of this size
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   if (tid < 64) {
     int cnt = 0, big = 0;
