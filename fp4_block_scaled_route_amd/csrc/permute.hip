@@ -22,9 +22,8 @@
 // order.  The group offsets also give the processing order of the groups for
 // the GEMM (non-empty groups, largest first by a counting sort over the
 // sizes, ties by id), so that the GEMM grid needs no host synchronisation.
-// Extra workgroups compute the per-row
-// staging shifts of the bf16 activations and clear the row-max buffer of the
-// hidden activations.
+// Extra workgroups compute the per-row staging shifts of the bf16 activations
+// and clear the row-max buffer of the hidden activations.
 #include <algorithm>
 
 #include "device_util.h"

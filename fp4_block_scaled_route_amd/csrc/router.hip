@@ -149,7 +149,8 @@ __device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi
 }
 template <int R>
 __device__ __forceinline__ void row_ror_step(float& bv, int& bi) {
-  // DPP row_ror:R (lane l of a 16-lane row reads lane (l + R) % 16 of that row)
+  // DPP row_ror:R: every lane reads the lane R places away, rotating within its
+  // 16-lane row (after rotations by 8, 4, 2 and 1 each lane has seen its whole row)
   const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), 0x120 + R, 0xF, 0xF, false));
   const int oi = __builtin_amdgcn_update_dpp(0, bi, 0x120 + R, 0xF, 0xF, false);
   take_better(bv, bi, ov, oi);
