@@ -371,14 +371,26 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
           ab = fmaxf(ab, __shfl_xor(ab, 16));
           ab = fmaxf(ab, __shfl_xor(ab, 32));
           const float gs = a.h_gs[0];
+          // Scale byte and codes on the hardware converters, which give the
+          // software encoders' bytes for every input but a NaN (see
+          // quant_block16): a lane whose values or reciprocal scale are not
+          // finite takes the software encoders.
           uint32_t sbyte = 0, packed = 0;
           if (gs != 0.0f) {
-            sbyte = e4m3_encode_nonneg(ab / (6.0f * gs));
+            sbyte = e4m3_encode_hw(ab / (6.0f * gs));
             const float scale = e4m3_to_float(sbyte) * gs;
             if (scale != 0.0f) {
               const float rcp = 1.0f / scale;
+              uint32_t im = 0;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) packed |= e2m1_encode(hv[i] * rcp) << (4 * i);
+              for (int i = 0; i < 4; ++i) im = max(im, __float_as_uint(hv[i]) & 0x7FFFFFFFu);
+              if (im < 0x7F800000u && rcp <= 3.402823466e38f) {
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, hv[0] * rcp, hv[1] * rcp, 1.0f, 0);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, hv[2] * rcp, hv[3] * rcp, 1.0f, 1) & 0xFFFFu;
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) packed |= e2m1_encode(hv[i] * rcp) << (4 * i);
+              }
             }
           }
           if (tv) {
