@@ -289,9 +289,13 @@ __device__ __forceinline__ void transpose4(u32x4& v) {
 // Epilogue for one pass.  acc[f][c]: fragment f, token chunk c; lane holds
 // D rows 4*lg..4*lg+3 of the fragment for token row pbase + 16c + lr.
 // Rows at or past `mlim` (end of this pass) are not written.
+// hgs: the global scale of the NVFP4 h (EPI_SWIGLU_FP4), read by the caller
+// before its first store: read here, between the stores, it would have to
+// wait for them (the compiler cannot rule out that they alias it).
 template <int R, int MAXC, int EP, int NW>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, const Frags<R, EP, NW>& fr,
-                                         f32x4 (&acc)[R][MAXC], int nc, int pbase, int mlim, int lr, int lg) {
+                                         f32x4 (&acc)[R][MAXC], int nc, int pbase, int mlim, int lr, int lg,
+                                         float hgs) {
   if constexpr (EP == EPI_PART_F32) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
@@ -370,7 +374,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
                            fmaxf(__builtin_fabsf(hv[2]), __builtin_fabsf(hv[3])));
           ab = fmaxf(ab, __shfl_xor(ab, 16));
           ab = fmaxf(ab, __shfl_xor(ab, 32));
-          const float gs = a.h_gs[0];
+          const float gs = hgs;
           // Scale byte and codes on the hardware converters, which give the
           // software encoders' bytes for every input but a NaN (see
           // quant_block16): a lane whose values or reciprocal scale are not
@@ -453,6 +457,7 @@ void nvfp4_gemm_compact(const GemmArgs a) {
   if (!resolve_item(a, gi0, it)) return;
   Frags<R, EP> fr;
   fr.init(a, it, nbk, wave, lr, lg);
+  const float hgs = EP == EPI_SWIGLU_FP4 ? a.h_gs[0] : 0.0f;
   const int K = a.K;
   // chunks of this item: [kbase, kbase + nkc) (all of K unless K is split)
   const int nkc = K / kChunk / (a.ksplit > 1 ? a.ksplit : 1);
@@ -560,7 +565,7 @@ void nvfp4_gemm_compact(const GemmArgs a) {
         }
       }
     }
-    epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, pbase + prow, lr, lg);
+    epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, pbase + prow, lr, lg, hgs);
   }
 }
 
@@ -590,6 +595,7 @@ void nvfp4_gemm_direct(const GemmArgs a) {
   if (!resolve_item(a, gi0, it)) return;
   Frags<R, EP> fr;
   fr.init(a, it, nbk, wave, lr, lg);
+  const float hgs = EP == EPI_SWIGLU_FP4 ? a.h_gs[0] : 0.0f;
   const int K = a.K;
   const int nkc = K / kChunk;
 
@@ -689,7 +695,7 @@ void nvfp4_gemm_direct(const GemmArgs a) {
       }
       fr.load(wb1, min(kc + 3, last), past(kc + 3));
     }
-    epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, min(it.m, pbase + 16), lr, lg);
+    epilogue<R, 1, EP, kNW>(a, it, fr, acc, 1, pbase, min(it.m, pbase + 16), lr, lg, hgs);
   }
 }
 
@@ -719,6 +725,9 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   // every thread writes its rows (the rows past PR hold zeros nobody reads),
   // so no wave-dependent branch separates the loads from their uses
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][SROWS * RSTEP * kLdsRow];
+  // Down GEMM, eight waves: pair ids of the pass's rows (see the epilogue)
+  constexpr bool SLOT_TILE = EP == EPI_SLOT && NW == 8 && R == 4;
+  __shared__ int s_pid[SLOT_TILE ? PR : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -743,6 +752,7 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
   if (!resolve_item(a, gi, it)) return;
   Frags<R, EP, NW> fr;
   fr.init(a, it, nbk, wave, lr, lg);
+  const float hgs = EP == EPI_SWIGLU_FP4 ? a.h_gs[0] : 0.0f;
   const int K = a.K;
   // chunks of this item: [kbase, kbase + nkc) (all of K unless K is split)
   const int nkc = K / kChunk / (a.ksplit > 1 ? a.ksplit : a.mks > 1 ? a.mks : 1);
@@ -919,6 +929,13 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       }
     };
 
+    // Down GEMM, eight waves: the pair id of each row of the pass, requested
+    // first and parked in LDS with the first chunk, for the epilogue's
+    // stores (a read there would wait for the stores before it).
+    int pidv = 0;
+    if constexpr (SLOT_TILE) {
+      if (tid < prow) pidv = a.perm[it.row0 + pbase + tid];
+    }
     // requests for chunks past the end carry kPast (no memory access, unused)
     if constexpr (QUAD) {
       fr.load_codes(wb.c0, wb.c1, 0);
@@ -928,6 +945,9 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
     }
     stage_load(0);
     stage_write(0);
+    if constexpr (SLOT_TILE) {
+      if (tid < prow) s_pid[tid] = pidv;
+    }
     __syncthreads();
     // Even chunks in LDS buffer 0, odd ones in buffer 1; every chunk stages
     // the next one (past the end: zeros, into the buffer no wave reads any
@@ -1059,13 +1079,13 @@ __global__ __launch_bounds__(NW * 64) void nvfp4_gemm_lds(const GemmArgs a) {
       __syncthreads();
       const int n0 = nbk * 512 + lane * 8;
       for (int tr = wave; tr < prow; tr += NW) {
-        const int pid = a.perm[it.row0 + pbase + tr];
+        const int pid = s_pid[tr];
         const u32x4 o = *reinterpret_cast<const u32x4*>(tile + tr * kTilePitch + lane * 16);
         if (n0 < a.N) *reinterpret_cast<u32x4*>(a.slot + (int64_t)pid * a.N + n0) = o;
       }
       if (pass + 1 < npass) __syncthreads();   // the next pass stages into these buffers
     } else {
-      epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg);
+      epilogue<R, MAXC, EP, NW>(a, it, fr, acc, nc, pbase, pbase + prow, lr, lg, hgs);
     }
   }
 }
