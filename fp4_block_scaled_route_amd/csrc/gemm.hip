@@ -323,24 +323,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
       const int r = it.row0 + tr;
       const int arow = a_row_of(a, r);
       const int sh = shift_of(a, arow);
+      // The row's values of every fragment first, then its stores back to
+      // back: the pair id is read before the first store and no register of
+      // a store is rewritten before the next one, so no store waits for
+      // another (output row = activation row for the dense and grouped
+      // linear, t * G + g for the latter; the pair's slot row for the MoE).
+      uint16_t* const yrow = EP == EPI_Y_BF16 ? a.y + (int64_t)arow * a.N : a.slot + (int64_t)a.perm[r] * a.N;
+      uint2 o[R];
 #pragma unroll
       for (int f = 0; f < R; ++f) {
-        if (!fr.fvalid[f]) continue;
-        const int n0 = fr.fbase[f] + 4 * lg;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh) * it.alpha;
-        uint2 o;
-        o.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
-        o.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
-        if constexpr (EP == EPI_Y_BF16) {
-          // output row = activation row (dense: r; grouped linear: t * G + g)
-          *reinterpret_cast<uint2*>(a.y + (int64_t)arow * a.N + n0) = o;
-        } else {
-          const int pid = a.perm[r];
-          *reinterpret_cast<uint2*>(a.slot + (int64_t)pid * a.N + n0) = o;
-        }
+        o[f].x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+        o[f].y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
       }
+#pragma unroll
+      for (int f = 0; f < R; ++f)
+        if (fr.fvalid[f]) *reinterpret_cast<uint2*>(yrow + fr.fbase[f] + 4 * lg) = o[f];
     }
   } else {
     // SwiGLU: fragments 2p (gate rows) and 2p+1 (up rows) share the layout
