@@ -296,23 +296,36 @@ template <int R, int MAXC, int EP, int NW>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, const Frags<R, EP, NW>& fr,
                                          f32x4 (&acc)[R][MAXC], int nc, int pbase, int mlim, int lr, int lg,
                                          float hgs) {
+  // Per token chunk c, for this lane's row of the pass: its activation row,
+  // power-of-two shift and (EPI_SLOT) pair id, all read before the first
+  // store for the reason given for hgs.
+  int arow[MAXC], sh[MAXC], pid[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int tr = pbase + 16 * c + lr;
+    const bool ok = c < nc && tr < mlim;
+    arow[c] = ok ? a_row_of(a, it.row0 + tr) : 0;
+    sh[c] = ok ? shift_of(a, arow[c]) : 0;
+    pid[c] = EP == EPI_SLOT && ok ? a.perm[it.row0 + tr] : 0;
+  }
+  // (one wait for them here, while no store is in flight: the compiler
+  // would otherwise wait at each use after a branch, with stores pending)
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   if constexpr (EP == EPI_PART_F32) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int tr = pbase + 16 * c + lr;
       if (c >= nc || tr >= mlim) continue;
-      const int arow = a_row_of(a, it.row0 + tr);
-      const int sh = shift_of(a, arow);
 #pragma unroll
       for (int f = 0; f < R; ++f) {
         if (!fr.fvalid[f]) continue;
         const int n0 = fr.fbase[f] + 4 * lg;
         float4 v;
-        v.x = __builtin_ldexpf(acc[f][c][0], -sh) * it.alpha;
-        v.y = __builtin_ldexpf(acc[f][c][1], -sh) * it.alpha;
-        v.z = __builtin_ldexpf(acc[f][c][2], -sh) * it.alpha;
-        v.w = __builtin_ldexpf(acc[f][c][3], -sh) * it.alpha;
-        *reinterpret_cast<float4*>(a.part + ((int64_t)it.ks * a.a_rows + arow) * a.N + n0) = v;
+        v.x = __builtin_ldexpf(acc[f][c][0], -sh[c]) * it.alpha;
+        v.y = __builtin_ldexpf(acc[f][c][1], -sh[c]) * it.alpha;
+        v.z = __builtin_ldexpf(acc[f][c][2], -sh[c]) * it.alpha;
+        v.w = __builtin_ldexpf(acc[f][c][3], -sh[c]) * it.alpha;
+        *reinterpret_cast<float4*>(a.part + ((int64_t)it.ks * a.a_rows + arow[c]) * a.N + n0) = v;
       }
     }
   } else if constexpr (EP == EPI_Y_BF16 || EP == EPI_SLOT) {
@@ -320,21 +333,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
     for (int c = 0; c < MAXC; ++c) {
       const int tr = pbase + 16 * c + lr;
       if (c >= nc || tr >= mlim) continue;
-      const int r = it.row0 + tr;
-      const int arow = a_row_of(a, r);
-      const int sh = shift_of(a, arow);
       // The row's values of every fragment first, then its stores back to
-      // back: the pair id is read before the first store and no register of
-      // a store is rewritten before the next one, so no store waits for
-      // another (output row = activation row for the dense and grouped
-      // linear, t * G + g for the latter; the pair's slot row for the MoE).
-      uint16_t* const yrow = EP == EPI_Y_BF16 ? a.y + (int64_t)arow * a.N : a.slot + (int64_t)a.perm[r] * a.N;
+      // back, so that no register of a store is rewritten before the next
+      // one (output row = activation row for the dense and grouped linear,
+      // t * G + g for the latter; the pair's slot row for the MoE).
+      uint16_t* const yrow = EP == EPI_Y_BF16 ? a.y + (int64_t)arow[c] * a.N : a.slot + (int64_t)pid[c] * a.N;
       uint2 o[R];
 #pragma unroll
       for (int f = 0; f < R; ++f) {
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh) * it.alpha;
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_ldexpf(acc[f][c][i], -sh[c]) * it.alpha;
         o[f].x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
         o[f].y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
       }
@@ -350,7 +359,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
       const int tr = pbase + 16 * c + lr;
       const bool tv = tr < mlim;
       const int r = it.row0 + (tv ? tr : 0);
-      const int sh = tv ? shift_of(a, a_row_of(a, r)) : 0;
       float hmx = 0.f;
 #pragma unroll
       for (int p = 0; p < R / 2; ++p) {
@@ -359,8 +367,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Item& it, cons
         float hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float gv = __builtin_ldexpf(acc[2 * p][c][i], -sh) * it.alpha;
-          const float uv = __builtin_ldexpf(acc[2 * p + 1][c][i], -sh) * it.alpha;
+          const float gv = __builtin_ldexpf(acc[2 * p][c][i], -sh[c]) * it.alpha;
+          const float uv = __builtin_ldexpf(acc[2 * p + 1][c][i], -sh[c]) * it.alpha;
           hv[i] = gv / (1.0f + __expf(-gv)) * uv;
         }
         if constexpr (EP == EPI_SWIGLU_F32) {
