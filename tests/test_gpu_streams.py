@@ -2,9 +2,12 @@
 
 The result must not depend on the stream the call is made on; the call must
 be capturable into a graph and give the same result on every replay, with
-eager work between the replays; the stage events are recorded in order.  The eager result is checked against the
-oracle, the stream and graph runs bit for bit against it (the arithmetic of
-every output row is fixed by the routing and the inputs)."""
+eager work between the replays; the stage events are recorded in order.  The
+eager result of the small case is checked against the oracle, the stream and
+graph runs bit for bit against the eager result (the arithmetic of every
+output row is fixed by the routing and the inputs); the large-batch path's
+parity with the oracle is the MoE parity tests' part, here its replays are
+compared with its eager call."""
 import ctypes
 
 import numpy as np
@@ -108,3 +111,46 @@ def test_moe_stage_events_in_order():
     assert torch.equal(y, y2)
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def test_moe_fully_fp4_large_batch_graph_replay():
+    """The large-batch path (every group on the eight-wave kernel, NVFP4
+    activations and NVFP4 h, groups of more than one 112-row pass) captured
+    into a graph: every replay equals the eager call bit for bit."""
+    t, h, i, e, k = 600, 1024, 1024, 16, 4       # 150 rows a group on average, shared expert 600 rows
+    say(f"fully-FP4 large batch captured into a graph T={t} H={h} I={i} E={e} k={k}")
+    mi = synth.make_moe(t, h, i, e, k, seed=23, routing="uniform", shared=True, threads=2)
+    de, ds = DeviceExperts(mi.experts), DeviceExperts(mi.shared)
+    xq, xs, gs = ops.quantize_act(dev(mi.x))
+    ids, w = dev(mi.topk_ids), dev(mi.topk_w)
+    # the hidden activations' global scale from the fp32-h path of the same call
+    a2 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.moe_grouped(ids, w, **de.args(), x_fp4=xq, x_sf=xs, a1_gs=gs, shared=ds.as_shared(), a2_gs_out=a2)
+    torch.cuda.synchronize()
+    assert float(a2.item()) > 0.0
+    ws = torch.empty(ops.moe_workspace_size(t, h, i, e, k, True, True), dtype=torch.uint8, device="cuda")
+    args = dict(topk_ids=ids, topk_w=w, **de.args(), x_fp4=xq, x_sf=xs, a1_gs=gs, shared=ds.as_shared(),
+                a2_gs=a2, workspace=ws)
+    y0 = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
+    ops.moe_grouped(**args, out=y0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y0.float()).all() and y0.float().abs().max() > 0
+    s = torch.cuda.Stream()
+    yg = torch.zeros_like(y0)
+    with torch.cuda.stream(s):
+        ops.moe_grouped(**args, out=yg)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ops.moe_grouped(**args, out=yg)
+    torch.cuda.synchronize()
+    ws2 = torch.empty_like(ws)
+    other = torch.empty_like(y0)
+    for rep in range(3):
+        yg.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y0), f"replay {rep} differs from the eager result"
+        ops.moe_grouped(**{**args, "workspace": ws2}, out=other)
+        torch.cuda.synchronize()
+        assert torch.equal(other, y0)
